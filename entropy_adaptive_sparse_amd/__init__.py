@@ -1,0 +1,217 @@
+"""Token Radius Attention (TRA) hot path for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libtra.so`` (declared in include/tra.h).
+It only marshals arguments: it checks tensor shapes/dtypes/devices, allocates
+outputs with torch when the caller passes none, and forwards raw device pointers
+and the current HIP stream.  Every step of the computation runs in the HIP
+kernels; there is no fallback of any kind -- if the library is missing, every
+call raises.
+
+Functions (names as in the C ABI, without the ``tra_`` prefix):
+    tile_major_permute / tile_major_unpermute
+    dense_attn_entropy
+    build_block_mask, mask_prepare
+    block_sparse_attn
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "TraError", "library_path", "load", "tile_major_permute", "tile_major_unpermute", "dense_attn_entropy",
+    "build_block_mask", "mask_prepare", "block_sparse_attn", "exported_symbols",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIBPATH = os.path.join(_HERE, "libtra.so")
+_lock = threading.Lock()
+_lib = None
+
+TRA_F32, TRA_BF16 = 0, 1
+_STATUS = {0: "TRA_OK", 1: "TRA_ERR_INVALID_ARG", 2: "TRA_ERR_UNSUPPORTED", 3: "TRA_ERR_HIP", 4: "TRA_ERR_CAPACITY"}
+
+
+class TraError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__("%s failed: %s (%d)" % (fn, _STATUS.get(code, "?"), code))
+        self.code = code
+
+
+def library_path() -> str:
+    return _LIBPATH
+
+
+def load():
+    """Load libtra.so (once).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIBPATH):
+            raise RuntimeError("libtra.so is not built (%s); run `python -m entropy_adaptive_sparse_amd.build`"
+                               % _LIBPATH)
+        lib = ctypes.CDLL(_LIBPATH)
+        P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        lib.tra_status_string.argtypes = [i32]
+        lib.tra_status_string.restype = ctypes.c_char_p
+        perm_args = [P, P, i32, i32, i32, i32, i32, i32, i32, i32, P]
+        lib.tra_tile_major_permute.argtypes = perm_args
+        lib.tra_tile_major_unpermute.argtypes = perm_args
+        lib.tra_dense_attn_entropy.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, f32, P]
+        lib.tra_build_block_mask.argtypes = [P, i32, i32, i32, i32, f32, f32, i32, i32, i32, i32, i32, P, P, i64,
+                                             P, P]
+        lib.tra_mask_prepare.argtypes = [i32, i32, i32, f32, f32, i32, i32, i32, i32]
+        lib.tra_block_sparse_attn.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, f32, i32, i32, P]
+        for name in ("tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
+                     "tra_build_block_mask", "tra_mask_prepare", "tra_block_sparse_attn"):
+            getattr(lib, name).restype = i32
+        _lib = lib
+        return lib
+
+
+def exported_symbols():
+    return ["tra_status_string", "tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
+            "tra_build_block_mask", "tra_mask_prepare", "tra_block_sparse_attn"]
+
+
+# ------------------------------------------------------------------------------------------------
+# marshalling helpers (torch is used only for device memory and the current stream)
+# ------------------------------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return TRA_F32
+    if t.dtype == torch.bfloat16:
+        return TRA_BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t) -> int:
+    return _torch().cuda.current_stream(t.device).cuda_stream
+
+
+def _call(fn: str, *args) -> None:
+    rc = getattr(load(), fn)(*args)
+    if rc != 0:
+        raise TraError(fn, rc)
+
+
+# ------------------------------------------------------------------------------------------------
+# entry points
+# ------------------------------------------------------------------------------------------------
+def tile_major_permute(x, F: int, H: int, W: int, tile_h: int = 8, tile_w: int = 8, out=None):
+    """x [outer][N][row] (natural order) -> y in tile-major order.  Also accepts [outer][N]."""
+    _dev(x, "x")
+    y = _torch().empty_like(x) if out is None else _dev(out, "out")
+    outer, N = x.shape[0], x.shape[1]
+    row = 1 if x.dim() == 2 else int(x[0, 0].numel())
+    if N != F * H * W or y.shape != x.shape or y.dtype != x.dtype:
+        raise ValueError("shape mismatch")
+    _call("tra_tile_major_permute", _ptr(x), _ptr(y), outer, F, H, W, row, _dt(x), tile_h, tile_w, _stream(x))
+    return y
+
+
+def tile_major_unpermute(y, F: int, H: int, W: int, tile_h: int = 8, tile_w: int = 8, out=None):
+    """y [outer][N][row] (tile-major) -> x in natural order."""
+    _dev(y, "y")
+    x = _torch().empty_like(y) if out is None else _dev(out, "out")
+    outer, N = y.shape[0], y.shape[1]
+    row = 1 if y.dim() == 2 else int(y[0, 0].numel())
+    if N != F * H * W or x.shape != y.shape or x.dtype != y.dtype:
+        raise ValueError("shape mismatch")
+    _call("tra_tile_major_unpermute", _ptr(y), _ptr(x), outer, F, H, W, row, _dt(y), tile_h, tile_w, _stream(y))
+    return x
+
+
+def _check_qkv(q, k, v):
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+        if t.dim() != 3:
+            raise ValueError("%s must be [outer][N][D]" % n)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share shape and dtype")
+    return q.shape
+
+
+def dense_attn_entropy(q, k, v, sm_scale: float | None = None, entropy: bool = True, lse: bool = False,
+                       out=None, ent_out=None, lse_out=None):
+    """Dense attention over all N keys with the per-query entropy (nats).  Returns (o, H, lse)."""
+    torch = _torch()
+    outer, N, D = _check_qkv(q, k, v)
+    o = torch.empty_like(q) if out is None else _dev(out, "out")
+    H = None
+    if entropy:
+        H = torch.empty((outer, N), dtype=torch.float32, device=q.device) if ent_out is None else ent_out
+    L = None
+    if lse:
+        L = torch.empty((outer, N), dtype=torch.float32, device=q.device) if lse_out is None else lse_out
+    scale = (1.0 / D ** 0.5) if sm_scale is None else float(sm_scale)
+    _call("tra_dense_attn_entropy", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(H), _ptr(L), outer, N, D, _dt(q),
+          scale, _stream(q))
+    return o, H, L
+
+
+def mask_prepare(F, H, W, tau, gamma, block_q=128, block_k=64, tile_h=8, tile_w=8) -> None:
+    _call("tra_mask_prepare", F, H, W, float(tau), float(gamma), block_q, block_k, tile_h, tile_w)
+
+
+def build_block_mask(entropy, F: int, H: int, W: int, tau: float, gamma: float, block_q: int = 128,
+                     block_k: int = 64, vote_threshold: int = 1, tile_h: int = 8, tile_w: int = 8,
+                     want_mask: bool = False, kv_count=None, kv_index=None, block_mask=None):
+    """entropy fp32 [outer][N] (tile-major) -> (kv_count [outer][nqb], kv_index [outer][nqb][nkb], mask|None)."""
+    torch = _torch()
+    _dev(entropy, "entropy")
+    if entropy.dtype != torch.float32 or entropy.dim() != 2:
+        raise ValueError("entropy must be float32 [outer][N]")
+    outer, N = entropy.shape
+    nqb, nkb = -(-N // block_q), -(-N // block_k)
+    dev = entropy.device
+    cnt = torch.empty((outer, nqb), dtype=torch.int32, device=dev) if kv_count is None else kv_count
+    idx = torch.empty((outer, nqb, nkb), dtype=torch.int32, device=dev) if kv_index is None else kv_index
+    msk = block_mask
+    if want_mask and msk is None:
+        msk = torch.empty((outer, nqb, nkb), dtype=torch.uint8, device=dev)
+    _call("tra_build_block_mask", _ptr(entropy), outer, F, H, W, float(tau), float(gamma), block_q, block_k,
+          int(vote_threshold), tile_h, tile_w, _ptr(cnt), _ptr(idx), idx.numel(), _ptr(msk), _stream(entropy))
+    return cnt, idx, msk
+
+
+def block_sparse_attn(q, k, v, kv_count, kv_index, block_q: int = 128, block_k: int = 64,
+                      sm_scale: float | None = None, lse: bool = False, out=None, lse_out=None):
+    """Attention of each query over the tokens of its q-block's retained k-blocks.  Returns (o, lse)."""
+    torch = _torch()
+    outer, N, D = _check_qkv(q, k, v)
+    _dev(kv_count, "kv_count")
+    _dev(kv_index, "kv_index")
+    nqb, nkb = -(-N // block_q), -(-N // block_k)
+    if tuple(kv_count.shape) != (outer, nqb) or tuple(kv_index.shape) != (outer, nqb, nkb):
+        raise ValueError("kv_count/kv_index shape does not match N, block_q, block_k")
+    if kv_count.dtype != torch.int32 or kv_index.dtype != torch.int32:
+        raise ValueError("kv_count/kv_index must be int32")
+    o = torch.empty_like(q) if out is None else _dev(out, "out")
+    L = None
+    if lse:
+        L = torch.empty((outer, N), dtype=torch.float32, device=q.device) if lse_out is None else lse_out
+    scale = (1.0 / D ** 0.5) if sm_scale is None else float(sm_scale)
+    _call("tra_block_sparse_attn", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), _ptr(kv_count), _ptr(kv_index),
+          outer, N, D, _dt(q), scale, block_q, block_k, _stream(q))
+    return o, L

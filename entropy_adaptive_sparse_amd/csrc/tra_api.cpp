@@ -1,0 +1,320 @@
+// tra_api.cpp -- the C ABI of libtra.so: argument validation (before any HIP call),
+// the per-device cache of mask tables, and dispatch to the HIP kernels.
+//
+// The host-built tables follow "Token Radius Attention for Efficient Video
+// Generation", section 2 (Insight I budget tau * exp(H_i) / N, Insight II radius
+// with per-frame factor exp(-gamma * delta)); the disk test is evaluated on the
+// device as an integer comparison against these fp64 tables.
+#include "../../include/tra.h"
+#include "tra_internal.h"
+
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+#include <tuple>
+#include <vector>
+
+namespace {
+
+using tra::TileGeom;
+
+constexpr int64_t kMaxN = (int64_t)1 << 30;
+
+bool valid_dtype(tra_dtype dt) { return dt == TRA_F32 || dt == TRA_BF16; }
+int64_t dtype_bytes(tra_dtype dt) { return dt == TRA_F32 ? 4 : 2; }
+
+tra_status check_grid(int F, int H, int W, int tile_h, int tile_w, TileGeom &g) {
+    if (F < 1 || H < 1 || W < 1 || tile_h < 1 || tile_w < 1) return TRA_ERR_INVALID_ARG;
+    const int64_t N = (int64_t)F * H * W;
+    if (N > kMaxN || (int64_t)tile_h * W > kMaxN) return TRA_ERR_UNSUPPORTED;
+    g.F = F; g.H = H; g.W = W; g.th = tile_h; g.tw = tile_w;
+    g.HW = H * W;
+    g.N = (int)N;
+    return TRA_OK;
+}
+
+// ------------------------------------------------------------------ mask tables
+// lambda[f][f'] = (ln tau - (2 gamma)|f - f'|) - ln(pi * S_f), S_f summed over f' in
+// increasing order; lnT[t] = ln t.  Written with separately rounded fp64 operations
+// (no contraction) so the tables are reproducible bit for bit with the C library.
+#pragma clang fp contract(off)
+void build_lambda(int F, double tau, double gamma, std::vector<double> &lam) {
+    std::vector<double> S((size_t)F);
+    for (int f = 0; f < F; ++f) {
+        double acc = 0.0;
+        for (int fp = 0; fp < F; ++fp) {
+            const int delta = f > fp ? f - fp : fp - f;
+            acc += std::exp(-(2.0 * gamma) * (double)delta);
+        }
+        S[(size_t)f] = acc;
+    }
+    lam.resize((size_t)F * F);
+    for (int f = 0; f < F; ++f)
+        for (int fp = 0; fp < F; ++fp) {
+            const int delta = f > fp ? f - fp : fp - f;
+            lam[(size_t)f * F + fp] = (std::log(tau) - (2.0 * gamma) * (double)delta) - std::log(M_PI * S[(size_t)f]);
+        }
+}
+
+void build_log_table(int tmax, std::vector<double> &lnT) {
+    lnT.resize((size_t)tmax + 1);
+    lnT[0] = -INFINITY;
+    for (int t = 1; t <= tmax; ++t) lnT[(size_t)t] = std::log((double)t);
+}
+#pragma clang fp contract(on)
+
+// k-block kb = tile-major positions [kb*bk, min(N, kb*bk + bk)) as a union of
+// axis-aligned rectangles in (frame, row, column): maximal runs along a row are
+// merged with the run directly above them when they span the same columns.
+void build_rects(const TileGeom &g, int bk, std::vector<int32_t> &off, std::vector<int4> &rects) {
+    const int nkb = (g.N + bk - 1) / bk;
+    off.assign((size_t)nkb + 1, 0);
+    rects.clear();
+    for (int kb = 0; kb < nkb; ++kb) {
+        off[(size_t)kb] = (int32_t)rects.size();
+        const int p0 = kb * bk, p1 = std::min(g.N, p0 + bk);
+        const size_t first = rects.size();
+        int p = p0;
+        while (p < p1) {
+            int f, y, x;
+            tra::tile_major_coords(p, g, f, y, x);
+            int x1 = x;
+            int q = p + 1;
+            while (q < p1) {
+                int f2, y2, xx2;
+                tra::tile_major_coords(q, g, f2, y2, xx2);
+                if (f2 != f || y2 != y || xx2 != x1 + 1) break;
+                x1 = xx2;
+                ++q;
+            }
+            // merge with an earlier rectangle of this block that ends on the row above
+            bool merged = false;
+            for (size_t r = first; r < rects.size(); ++r) {
+                int4 &rc = rects[r];
+                const int ry1 = rc.y >> 16, rx0 = rc.z & 0xffff, rx1 = rc.z >> 16;
+                if (rc.x == f && ry1 == y - 1 && rx0 == x && rx1 == x1) {
+                    rc.y = (rc.y & 0xffff) | (y << 16);
+                    merged = true;
+                    break;
+                }
+            }
+            if (!merged) rects.push_back(make_int4(f, y | (y << 16), x | (x1 << 16), 0));
+            p = q;
+        }
+    }
+    off[(size_t)nkb] = (int32_t)rects.size();
+}
+
+struct TableKey {
+    int dev, F, H, W, bk, th, tw;
+    uint32_t tau_bits, gamma_bits;
+    bool operator<(const TableKey &o) const {
+        return std::tie(dev, F, H, W, bk, th, tw, tau_bits, gamma_bits) <
+               std::tie(o.dev, o.F, o.H, o.W, o.bk, o.th, o.tw, o.tau_bits, o.gamma_bits);
+    }
+};
+
+struct TableEntry {
+    void *mem = nullptr;
+    tra::MaskTables t{};
+};
+
+std::mutex g_mu;
+std::map<TableKey, TableEntry> g_tables;
+
+uint32_t fbits(float v) {
+    uint32_t b;
+    std::memcpy(&b, &v, 4);
+    return b;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+tra_status get_tables(const TileGeom &g, float tau, float gamma, int bk, tra::MaskTables &out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TRA_ERR_HIP;
+    const TableKey key{dev, g.F, g.H, g.W, bk, g.th, g.tw, fbits(tau), fbits(gamma)};
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_tables.find(key);
+    if (it != g_tables.end()) {
+        out = it->second.t;
+        return TRA_OK;
+    }
+    std::vector<double> lam, lnT;
+    std::vector<int32_t> off;
+    std::vector<int4> rects;
+    const int tmax = (g.H - 1) * (g.H - 1) + (g.W - 1) * (g.W - 1);
+    try {
+        build_lambda(g.F, (double)tau, (double)gamma, lam);
+        build_log_table(tmax, lnT);
+        build_rects(g, bk, off, rects);
+    } catch (const std::bad_alloc &) {
+        return TRA_ERR_CAPACITY;
+    }
+    const size_t b_lam = align256(lam.size() * sizeof(double));
+    const size_t b_lnT = align256(lnT.size() * sizeof(double));
+    const size_t b_off = align256(off.size() * sizeof(int32_t));
+    const size_t b_rect = align256(std::max<size_t>(1, rects.size()) * sizeof(int4));
+    std::vector<char> host(b_lam + b_lnT + b_off + b_rect, 0);
+    std::memcpy(host.data(), lam.data(), lam.size() * sizeof(double));
+    std::memcpy(host.data() + b_lam, lnT.data(), lnT.size() * sizeof(double));
+    std::memcpy(host.data() + b_lam + b_lnT, off.data(), off.size() * sizeof(int32_t));
+    if (!rects.empty())
+        std::memcpy(host.data() + b_lam + b_lnT + b_off, rects.data(), rects.size() * sizeof(int4));
+    void *mem = nullptr;
+    if (hipMalloc(&mem, host.size()) != hipSuccess) return TRA_ERR_HIP;
+    if (hipMemcpy(mem, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(mem);
+        return TRA_ERR_HIP;
+    }
+    TableEntry e;
+    e.mem = mem;
+    char *base = static_cast<char *>(mem);
+    e.t.lam = reinterpret_cast<const double *>(base);
+    e.t.lnT = reinterpret_cast<const double *>(base + b_lam);
+    e.t.rect_off = reinterpret_cast<const int32_t *>(base + b_lam + b_lnT);
+    e.t.rects = reinterpret_cast<const int4 *>(base + b_lam + b_lnT + b_off);
+    e.t.tmax = tmax;
+    g_tables.emplace(key, e);
+    out = e.t;
+    return TRA_OK;
+}
+
+tra_status check_mask_args(int F, int H, int W, float tau, float gamma, int block_q, int block_k, int tile_h,
+                           int tile_w, TileGeom &g) {
+    const tra_status st = check_grid(F, H, W, tile_h, tile_w, g);
+    if (st != TRA_OK) return st;
+    if (!(tau > 0.0f) || !std::isfinite(tau) || !(gamma >= 0.0f) || !std::isfinite(gamma))
+        return TRA_ERR_INVALID_ARG;
+    if (block_q < 1 || block_k < 1) return TRA_ERR_INVALID_ARG;
+    if ((block_q != 64 && block_q != 128) || block_k != 64) return TRA_ERR_UNSUPPORTED;
+    if (H > 32767 || W > 32767) return TRA_ERR_UNSUPPORTED;  // rectangle bounds are packed in 16 bits
+    const int64_t tmax = (int64_t)(H - 1) * (H - 1) + (int64_t)(W - 1) * (W - 1);
+    if (tmax > (int64_t)1 << 28) return TRA_ERR_UNSUPPORTED;
+    const int nkb = (g.N + block_k - 1) / block_k;
+    if (tra::mask_lds_bytes(block_q, F, nkb) > 65536) return TRA_ERR_UNSUPPORTED;
+    return TRA_OK;
+}
+
+tra_status check_attn_common(const void *q, const void *k, const void *v, const void *o, int outer, int N, int D,
+                             tra_dtype dt, float sm_scale) {
+    if (!q || !k || !v || !o) return TRA_ERR_INVALID_ARG;
+    if (outer < 1 || N < 1 || D < 1) return TRA_ERR_INVALID_ARG;
+    if (!valid_dtype(dt)) return TRA_ERR_INVALID_ARG;
+    if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale)) return TRA_ERR_INVALID_ARG;
+    if (o == q || o == k || o == v) return TRA_ERR_INVALID_ARG;
+    if (D != 64 && D != 128) return TRA_ERR_UNSUPPORTED;
+    if ((int64_t)N > kMaxN || (int64_t)outer * ((N + 63) / 64) > ((int64_t)1 << 31) - 1) return TRA_ERR_UNSUPPORTED;
+    const uintptr_t al = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o;
+    if (al % 16 != 0) return TRA_ERR_INVALID_ARG;  // rows are moved in 16-byte units
+    return TRA_OK;
+}
+
+tra_status from_hip(hipError_t e) { return e == hipSuccess ? TRA_OK : TRA_ERR_HIP; }
+
+tra_status permute_impl(const void *src, void *dst, int outer, int F, int H, int W, int row_elems, tra_dtype dt,
+                        int tile_h, int tile_w, hipStream_t s, int dir) {
+    if (!src || !dst || src == dst) return TRA_ERR_INVALID_ARG;
+    if (outer < 1 || row_elems < 1 || !valid_dtype(dt)) return TRA_ERR_INVALID_ARG;
+    TileGeom g;
+    const tra_status st = check_grid(F, H, W, tile_h, tile_w, g);
+    if (st != TRA_OK) return st;
+    if ((int64_t)outer * g.N > ((int64_t)1 << 40)) return TRA_ERR_UNSUPPORTED;
+    return from_hip(tra::launch_permute(src, dst, outer, g, (int64_t)row_elems * dtype_bytes(dt), dir, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *tra_status_string(tra_status st) {
+    switch (st) {
+        case TRA_OK: return "TRA_OK";
+        case TRA_ERR_INVALID_ARG: return "TRA_ERR_INVALID_ARG";
+        case TRA_ERR_UNSUPPORTED: return "TRA_ERR_UNSUPPORTED";
+        case TRA_ERR_HIP: return "TRA_ERR_HIP";
+        case TRA_ERR_CAPACITY: return "TRA_ERR_CAPACITY";
+    }
+    return "TRA_ERR_UNKNOWN";
+}
+
+tra_status tra_tile_major_permute(const void *x, void *y, int outer, int F, int H, int W, int row_elems,
+                                  tra_dtype dt, int tile_h, int tile_w, hipStream_t s) {
+    return permute_impl(x, y, outer, F, H, W, row_elems, dt, tile_h, tile_w, s, 0);
+}
+
+tra_status tra_tile_major_unpermute(const void *y, void *x, int outer, int F, int H, int W, int row_elems,
+                                    tra_dtype dt, int tile_h, int tile_w, hipStream_t s) {
+    return permute_impl(y, x, outer, F, H, W, row_elems, dt, tile_h, tile_w, s, 1);
+}
+
+tra_status tra_dense_attn_entropy(const void *q, const void *k, const void *v, void *o, float *entropy, float *lse,
+                                  int outer, int N, int D, tra_dtype dt, float sm_scale, hipStream_t s) {
+    const tra_status st = check_attn_common(q, k, v, o, outer, N, D, dt, sm_scale);
+    if (st != TRA_OK) return st;
+    tra::AttnArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    a.ent = entropy; a.lse = lse;
+    a.outer = outer; a.N = N;
+    a.nqb = (N + 127) / 128;
+    a.nkb = (N + 63) / 64;
+    a.sm_scale = sm_scale;
+    a.c = (float)((double)sm_scale * 1.4426950408889634074);
+    return from_hip(tra::launch_attention(a, D, dt == TRA_BF16 ? 1 : 0, 128, false, s));
+}
+
+tra_status tra_mask_prepare(int F, int H, int W, float tau, float gamma, int block_q, int block_k, int tile_h,
+                            int tile_w) {
+    TileGeom g;
+    const tra_status st = check_mask_args(F, H, W, tau, gamma, block_q, block_k, tile_h, tile_w, g);
+    if (st != TRA_OK) return st;
+    tra::MaskTables t;
+    return get_tables(g, tau, gamma, block_k, t);
+}
+
+tra_status tra_build_block_mask(const float *entropy, int outer, int F, int H, int W, float tau, float gamma,
+                                int block_q, int block_k, int vote_threshold, int tile_h, int tile_w,
+                                int32_t *kv_count, int32_t *kv_index, int64_t kv_index_capacity,
+                                uint8_t *block_mask, hipStream_t s) {
+    if (!entropy || !kv_count || !kv_index || outer < 1 || vote_threshold < 1) return TRA_ERR_INVALID_ARG;
+    TileGeom g;
+    const tra_status st = check_mask_args(F, H, W, tau, gamma, block_q, block_k, tile_h, tile_w, g);
+    if (st != TRA_OK) return st;
+    const int nqb = (g.N + block_q - 1) / block_q;
+    const int nkb = (g.N + block_k - 1) / block_k;
+    if ((int64_t)outer * nqb > ((int64_t)1 << 31) - 1) return TRA_ERR_UNSUPPORTED;
+    if (kv_index_capacity < (int64_t)outer * nqb * nkb) return TRA_ERR_CAPACITY;
+    tra::MaskArgs a{};
+    const tra_status ts = get_tables(g, tau, gamma, block_k, a.t);
+    if (ts != TRA_OK) return ts;
+    a.ent = entropy;
+    a.outer = outer; a.nqb = nqb; a.nkb = nkb;
+    a.block_q = block_q; a.block_k = block_k; a.vote = vote_threshold;
+    a.g = g;
+    a.kv_count = kv_count; a.kv_index = kv_index; a.block_mask = block_mask;
+    return from_hip(tra::launch_build_mask(a, s));
+}
+
+tra_status tra_block_sparse_attn(const void *q, const void *k, const void *v, void *o, float *lse,
+                                 const int32_t *kv_count, const int32_t *kv_index, int outer, int N, int D,
+                                 tra_dtype dt, float sm_scale, int block_q, int block_k, hipStream_t s) {
+    tra_status st = check_attn_common(q, k, v, o, outer, N, D, dt, sm_scale);
+    if (st != TRA_OK) return st;
+    if (!kv_count || !kv_index) return TRA_ERR_INVALID_ARG;
+    if (block_q < 1 || block_k < 1) return TRA_ERR_INVALID_ARG;
+    if ((block_q != 64 && block_q != 128) || block_k != 64) return TRA_ERR_UNSUPPORTED;
+    tra::AttnArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    a.ent = nullptr; a.lse = lse;
+    a.kv_count = kv_count; a.kv_index = kv_index;
+    a.outer = outer; a.N = N;
+    a.nqb = (N + block_q - 1) / block_q;
+    a.nkb = (N + block_k - 1) / block_k;
+    a.sm_scale = sm_scale;
+    a.c = (float)((double)sm_scale * 1.4426950408889634074);
+    return from_hip(tra::launch_attention(a, D, dt == TRA_BF16 ? 1 : 0, block_q, true, s));
+}
+
+}  // extern "C"

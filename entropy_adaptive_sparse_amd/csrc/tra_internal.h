@@ -1,0 +1,85 @@
+// tra_internal.h -- declarations shared by the C ABI layer and the HIP kernels of
+// libtra.so.  Not part of the public interface (include/tra.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tra {
+
+// Geometry of the latent grid and its tile-major order.
+struct TileGeom {
+    int F, H, W;      // frames, rows, columns
+    int th, tw;       // tile shape
+    int HW;           // H * W
+    int N;            // F * H * W
+};
+
+// Position p of the tile-major sequence -> (frame, row, column) of that token.
+// Tile-major order: frame, row of tiles, tile, row inside the tile, column inside
+// the tile; edge tiles clipped.
+__host__ __device__ inline void tile_major_coords(int p, const TileGeom &g, int &f, int &y, int &x) {
+    f = p / g.HW;
+    const int r = p - f * g.HW;
+    const int band = g.th * g.W;                 // tokens in one full row of tiles
+    const int ty = r / band;
+    const int r2 = r - ty * band;
+    const int ht = min(g.th, g.H - ty * g.th);   // rows in this row of tiles
+    const int tile = ht * g.tw;                  // tokens in a full-width tile of this row
+    const int tx = r2 / tile;
+    const int r3 = r2 - tx * tile;
+    const int wt = min(g.tw, g.W - tx * g.tw);   // columns in this tile
+    const int yy = r3 / wt;
+    y = ty * g.th + yy;
+    x = tx * g.tw + (r3 - yy * wt);
+}
+
+__host__ __device__ inline int tile_major_to_natural(int p, const TileGeom &g) {
+    int f, y, x;
+    tile_major_coords(p, g, f, y, x);
+    return (f * g.H + y) * g.W + x;
+}
+
+// ---------------------------------------------------------------- permute
+// dir = 0: y[o][p] = x[o][pi(p)]; dir = 1: x[o][pi(p)] = y[o][p].
+hipError_t launch_permute(const void *src, void *dst, int outer, const TileGeom &g, int64_t row_bytes,
+                          int dir, hipStream_t s);
+
+// ---------------------------------------------------------------- mask
+// Device-resident tables for one (geometry, tau, gamma, block_k, tile) key.
+struct MaskTables {
+    const double *lam;      // [F][F]  (ln tau - (2 gamma)|f - f'|) - ln(pi S_f)
+    const double *lnT;      // [tmax + 1], lnT[t] = ln t, lnT[0] = -inf
+    const int32_t *rect_off;// [nkb + 1]
+    const int4 *rects;      // {f, y0 | y1 << 16, x0 | x1 << 16, 0}, inclusive bounds
+    int tmax;               // (H-1)^2 + (W-1)^2
+};
+
+struct MaskArgs {
+    const float *ent;
+    int outer, nqb, nkb, block_q, block_k, vote;
+    TileGeom g;
+    MaskTables t;
+    int32_t *kv_count;
+    int32_t *kv_index;
+    uint8_t *block_mask;
+};
+
+hipError_t launch_build_mask(const MaskArgs &a, hipStream_t s);
+size_t mask_lds_bytes(int block_q, int F, int nkb);
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *ent, *lse;
+    const int32_t *kv_count, *kv_index;
+    int outer, N, nqb, nkb;
+    float c;          // sm_scale * log2(e)
+    float sm_scale;
+};
+
+// dtype: 0 = fp32, 1 = bf16.  sparse: walk kv_index; else every k-block (dense).
+hipError_t launch_attention(const AttnArgs &a, int D, int dtype, int block_q, bool sparse, hipStream_t s);
+
+}  // namespace tra

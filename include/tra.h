@@ -1,0 +1,164 @@
+/*
+ * tra.h -- C ABI of libtra.so, the MI355X (gfx950) hot path of Token Radius
+ * Attention (TRA).
+ *
+ * The method ("Token Radius Attention for Efficient Video Generation",
+ * gist.science summary of arXiv 2608.02504, section 2): a dense warm-up
+ * attention pass yields each query's softmax entropy H_i; the entropy maps to
+ * a token budget tau * exp(H_i) (Insight I), the budget to a query-centred
+ * spatial radius that shrinks with temporal distance by exp(-gamma * delta)
+ * (Insight II); tokens are laid out tile-major, a fused kernel turns the
+ * token-level disks into a regular block-sparse mask (distance computation,
+ * radius comparison, block pruning, token voting), and later denoising steps
+ * run block-sparse attention over that mask (TRA pipeline, steps 1-3).
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or keeps caller memory.
+ *  - Tensors are [outer][N][row] contiguous (outer = batch * heads), row-major.
+ *    Attention inputs and outputs, entropies and masks are in TILE-MAJOR token
+ *    order (see tra_tile_major_permute).
+ *  - Every call is asynchronous on the caller's stream `s` (0 = the null
+ *    stream) and returns once the work is enqueued.  Nothing on these paths
+ *    copies device data to the host.
+ *  - Arguments are validated before any HIP call: a bad argument returns
+ *    TRA_ERR_INVALID_ARG / TRA_ERR_UNSUPPORTED / TRA_ERR_CAPACITY and enqueues
+ *    nothing.  A failing HIP call returns TRA_ERR_HIP.  No C++ exception
+ *    crosses the ABI.
+ *  - Library state: a per-device cache of small fp64 tables and block
+ *    geometry for tra_build_block_mask, guarded by a mutex.  Its first use for
+ *    a geometry allocates and uploads them synchronously (tra_mask_prepare
+ *    does that ahead of time); entries live until the process ends.
+ */
+#ifndef TRA_H_
+#define TRA_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TRA_OK = 0,
+    TRA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, N != F*H*W, tau <= 0, ... */
+    TRA_ERR_UNSUPPORTED = 2, /* valid but not implemented: head dim, dtype or block shape */
+    TRA_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
+    TRA_ERR_CAPACITY = 4     /* an output buffer is smaller than the call needs */
+} tra_status;
+
+typedef enum { TRA_F32 = 0, TRA_BF16 = 1 } tra_dtype;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *tra_status_string(tra_status st);
+
+/*
+ * Tile-major permutation (TRA pipeline step 3, tile-major layout: tokens are
+ * reordered so that spatial neighbours are contiguous in the sequence).
+ *
+ * Token order: natural index (f*H + h)*W + w.  Tile-major order walks frame
+ * f, then rows of tiles, then tiles left to right, then rows inside the tile,
+ * then columns inside the tile; tiles are tile_h x tile_w, clipped at the
+ * bottom/right edges, never padded, so the map is a bijection on N = F*H*W.
+ *
+ *   permute:   y[o][p][:] = x[o][pi(p)][:]
+ *   unpermute: x[o][pi(p)][:] = y[o][p][:]
+ * where pi(p) is the natural index of the token at tile-major position p.
+ *
+ * x, y: device, [outer][N][row_elems] of `dt` (fp32 or bf16), distinct
+ * buffers (in-place is rejected).  row_elems = 1 reorders a per-token vector
+ * such as the entropies.  Pure data movement: bit-exact.
+ */
+tra_status tra_tile_major_permute(const void *x, void *y, int outer, int F, int H, int W, int row_elems,
+                                  tra_dtype dt, int tile_h, int tile_w, hipStream_t s);
+tra_status tra_tile_major_unpermute(const void *y, void *x, int outer, int F, int H, int W, int row_elems,
+                                    tra_dtype dt, int tile_h, int tile_w, hipStream_t s);
+
+/*
+ * Dense warm-up attention with fused per-query entropy (section 1: dense 3D
+ * self-attention over N video tokens; pipeline step 1: the entropy of every
+ * query is taken during the dense warm-up; section 3 contribution 3: the
+ * entropy kernel is fused to keep its overhead low).
+ *
+ *   o_i   = sum_j softmax_j(sm_scale * <q_i, k_j>) v_j      (all N keys, non-causal)
+ *   H_i   = -sum_j p_ij ln p_ij                               (nats)
+ *   lse_i = ln sum_j exp(sm_scale * <q_i, k_j>)
+ *
+ * q, k, v, o: device, [outer][N][D] of `dt` (the same dtype for all four);
+ * D in {64, 128}.  bf16 inputs are multiplied on bf16 matrix cores with fp32
+ * accumulation; softmax statistics and the entropy are fp32; fp32 inputs use
+ * fp32 matrix cores.  entropy, lse: device fp32 [outer][N], each may be NULL.
+ * o must not alias q, k or v.
+ */
+tra_status tra_dense_attn_entropy(const void *q, const void *k, const void *v, void *o, float *entropy,
+                                  float *lse, int outer, int N, int D, tra_dtype dt, float sm_scale,
+                                  hipStream_t s);
+
+/*
+ * Entropy -> budget -> radius -> block-sparse mask (Insight I: budget
+ * tau * exp(H_i) / N; Insight II: the budget becomes a query-specific base
+ * radius scaled per frame by phi(delta) = exp(-gamma * delta); pipeline
+ * steps 2-3: a 2D disk per frame, then a fused kernel doing distance
+ * computation, radius comparison, block pruning and token voting).
+ *
+ * Definition computed (bit-exact, no transcendental evaluated on the device):
+ * query i (tile-major position, frame f_i, spatial h_i, w_i) keeps key j iff
+ * d2 = (h_i - h_j)^2 + (w_i - w_j)^2 is 0, or
+ *      ln(d2) <= (double)H_i + lambda[f_i][f_j],
+ *      lambda[f][f'] = (ln tau - (2 gamma)|f - f'|) - ln(pi * S_f),
+ *      S_f = sum_{f'=0}^{F-1} exp(-2 gamma |f - f'|),
+ * with ln(d2) and lambda built in fp64 on the host with the C library.  This
+ * is the disk d2 <= (r_i exp(-gamma |f_i - f_j|))^2 whose base radius r_i
+ * makes the per-frame disk areas add up to the budget tau * exp(H_i).
+ * Blocks are contiguous ranges of the tile-major sequence (block_q for
+ * queries, block_k for keys; ragged last blocks).  votes(Qb, Kb) = number of
+ * queries of Qb whose disk meets Kb; Kb is retained iff
+ * votes >= vote_threshold or Kb overlaps Qb's own index range.
+ *
+ * entropy: device fp32 [outer][N], tile-major order (the warm-up entropies,
+ * reused across later steps).  N = F*H*W.  tau > 0, gamma >= 0 (finite),
+ * vote_threshold >= 1, block_q in {64, 128}, block_k = 64, tile >= 1.
+ * Outputs (device):
+ *   kv_count [outer][nqb]          number of retained k-blocks per q-block
+ *   kv_index [outer][nqb][nkb]     ascending retained k-block indices, row
+ *                                  stride nkb = ceil(N / block_k); entries
+ *                                  past kv_count are unspecified
+ *   block_mask [outer][nqb][nkb]   optional (may be NULL): 1 = retained
+ * kv_index_capacity is the number of int32 elements of kv_index; fewer than
+ * outer*nqb*nkb returns TRA_ERR_CAPACITY.  The first call for a geometry
+ * uploads tables synchronously (see tra_mask_prepare).
+ */
+tra_status tra_build_block_mask(const float *entropy, int outer, int F, int H, int W, float tau, float gamma,
+                                int block_q, int block_k, int vote_threshold, int tile_h, int tile_w,
+                                int32_t *kv_count, int32_t *kv_index, int64_t kv_index_capacity,
+                                uint8_t *block_mask, hipStream_t s);
+
+/* Builds and uploads the tables tra_build_block_mask needs for this geometry
+ * on the current device (blocking), so that a timed call does no upload. */
+tra_status tra_mask_prepare(int F, int H, int W, float tau, float gamma, int block_q, int block_k, int tile_h,
+                            int tile_w);
+
+/*
+ * Block-sparse attention over a kept mask (pipeline step 3: the regular
+ * block-sparse mask runs on a block-sparse attention backend; cross-step
+ * reuse: the mask from the warm-up entropies serves later denoising steps).
+ *
+ *   o_i = sum_{j in retained blocks of q-block(i)} softmax_j(sm_scale <q_i,k_j>) v_j
+ *
+ * over every token of each retained k-block, nothing else.  q, k, v, o as in
+ * tra_dense_attn_entropy (tile-major order); kv_count / kv_index as written
+ * by tra_build_block_mask for the same N, block_q, block_k (indices must be
+ * in [0, nkb), ascending, counts in [1, nkb]; a row with count 0 yields zeros).
+ * lse: optional fp32 [outer][N].  With every block retained the result equals
+ * tra_dense_attn_entropy's bit for bit (same tile order, same arithmetic).
+ */
+tra_status tra_block_sparse_attn(const void *q, const void *k, const void *v, void *o, float *lse,
+                                 const int32_t *kv_count, const int32_t *kv_index, int outer, int N, int D,
+                                 tra_dtype dt, float sm_scale, int block_q, int block_k, hipStream_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRA_H_ */

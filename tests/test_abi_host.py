@@ -1,0 +1,127 @@
+"""Host-only checks of the C ABI (no GPU needed): the library loads, exports every
+symbol include/tra.h declares, and rejects bad arguments with its status codes
+before making any HIP call (so these run in a GPU-less container)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tra.h")
+
+OK, INVALID, UNSUPPORTED, HIPERR, CAPACITY = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+FAKE2 = 0x20000
+FAKE3 = 0x30000
+FAKE4 = 0x40000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import entropy_adaptive_sparse_amd as tra
+    if not os.path.exists(tra.library_path()):
+        from entropy_adaptive_sparse_amd import build
+        build.build()
+    return tra.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tra_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
+              "tra_build_block_mask", "tra_block_sparse_attn", "tra_mask_prepare", "tra_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in ((0, b"TRA_OK"), (1, b"TRA_ERR_INVALID_ARG"), (2, b"TRA_ERR_UNSUPPORTED"),
+                       (3, b"TRA_ERR_HIP"), (4, b"TRA_ERR_CAPACITY"), (99, b"TRA_ERR_UNKNOWN")):
+        assert lib.tra_status_string(code) == name
+
+
+def test_permute_validation(lib):
+    f = lib.tra_tile_major_permute
+    assert f(None, FAKE, 1, 2, 3, 4, 8, BF16, 8, 8, None) == INVALID
+    assert f(FAKE, None, 1, 2, 3, 4, 8, BF16, 8, 8, None) == INVALID
+    assert f(FAKE, FAKE, 1, 2, 3, 4, 8, BF16, 8, 8, None) == INVALID  # in place
+    assert f(FAKE, FAKE2, 0, 2, 3, 4, 8, BF16, 8, 8, None) == INVALID
+    assert f(FAKE, FAKE2, 1, 0, 3, 4, 8, BF16, 8, 8, None) == INVALID
+    assert f(FAKE, FAKE2, 1, 2, 3, 4, 0, BF16, 8, 8, None) == INVALID
+    assert f(FAKE, FAKE2, 1, 2, 3, 4, 8, 7, 8, 8, None) == INVALID
+    assert f(FAKE, FAKE2, 1, 2, 3, 4, 8, BF16, 0, 8, None) == INVALID
+    assert f(FAKE, FAKE2, 1, 2048, 2048, 2048, 8, BF16, 8, 8, None) == UNSUPPORTED
+    assert lib.tra_tile_major_unpermute(FAKE, FAKE, 1, 2, 3, 4, 8, BF16, 8, 8, None) == INVALID
+
+
+def test_dense_validation(lib):
+    f = lib.tra_dense_attn_entropy
+    args = [FAKE, FAKE2, FAKE3, FAKE4, None, None, 2, 1024, 128, BF16, 0.088, None]
+    for i in range(4):
+        a = list(args)
+        a[i] = None
+        assert f(*a) == INVALID
+    a = list(args); a[3] = FAKE; assert f(*a) == INVALID         # o aliases q
+    a = list(args); a[6] = 0; assert f(*a) == INVALID
+    a = list(args); a[7] = 0; assert f(*a) == INVALID
+    a = list(args); a[8] = 96; assert f(*a) == UNSUPPORTED
+    a = list(args); a[9] = 5; assert f(*a) == INVALID
+    a = list(args); a[10] = 0.0; assert f(*a) == INVALID
+    a = list(args); a[10] = float("nan"); assert f(*a) == INVALID
+    a = list(args); a[0] = FAKE + 2; assert f(*a) == INVALID     # misaligned
+
+
+def _mask_args(**kw):
+    a = dict(ent=FAKE, outer=2, F=4, H=16, W=16, tau=1.0, gamma=0.5, bq=64, bk=64, vote=1, th=8, tw=8,
+             cnt=FAKE2, idx=FAKE3, cap=2 * 16 * 16, mask=None, s=None)
+    a.update(kw)
+    return list(a.values())
+
+
+def test_mask_validation(lib):
+    f = lib.tra_build_block_mask
+    assert f(*_mask_args(ent=None)) == INVALID
+    assert f(*_mask_args(cnt=None)) == INVALID
+    assert f(*_mask_args(idx=None)) == INVALID
+    assert f(*_mask_args(outer=0)) == INVALID
+    assert f(*_mask_args(F=0)) == INVALID
+    assert f(*_mask_args(tau=0.0)) == INVALID
+    assert f(*_mask_args(tau=-1.0)) == INVALID
+    assert f(*_mask_args(tau=float("inf"))) == INVALID
+    assert f(*_mask_args(gamma=-0.1)) == INVALID
+    assert f(*_mask_args(gamma=float("nan"))) == INVALID
+    assert f(*_mask_args(vote=0)) == INVALID
+    assert f(*_mask_args(bq=96)) == UNSUPPORTED
+    assert f(*_mask_args(bk=128)) == UNSUPPORTED
+    assert f(*_mask_args(th=0)) == INVALID
+    assert f(*_mask_args(cap=2 * 16 * 16 - 1)) == CAPACITY
+    assert f(*_mask_args(F=400, H=64, W=64, cap=10 ** 9)) == UNSUPPORTED  # LDS budget
+
+
+def test_sparse_validation(lib):
+    f = lib.tra_block_sparse_attn
+    base = [FAKE, FAKE2, FAKE3, FAKE4, None, FAKE + 4096, FAKE2 + 4096, 2, 1024, 128, BF16, 0.088, 128, 64, None]
+    a = list(base); a[5] = None; assert f(*a) == INVALID
+    a = list(base); a[6] = None; assert f(*a) == INVALID
+    a = list(base); a[12] = 32; assert f(*a) == UNSUPPORTED
+    a = list(base); a[13] = 32; assert f(*a) == UNSUPPORTED
+    a = list(base); a[12] = 0; assert f(*a) == INVALID
+    a = list(base); a[9] = 80; assert f(*a) == UNSUPPORTED
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    import entropy_adaptive_sparse_amd as tra
+    x = torch.zeros(1, 8, 4)
+    with pytest.raises(ValueError):
+        tra.tile_major_permute(x, 1, 2, 4)

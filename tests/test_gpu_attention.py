@@ -1,0 +1,260 @@
+"""GPU parity: dense warm-up attention + entropy, and block-sparse attention, against
+the fp64 oracle on the same (bf16- or fp32-valued) inputs ("Token Radius Attention
+for Efficient Video Generation", section 1; TRA pipeline steps 1 and 3).
+
+Tolerances: entropy <= 1e-3 nats absolute; outputs fp32 max-abs <= 1e-4, bf16
+relative L2 <= 1e-2 and max-abs <= 3e-2; lse <= 1e-3 absolute.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from entropy_adaptive_sparse_amd import synth, workloads
+from gpu_util import (check_output, device, qkv_inputs, say, sample_rows, small_workload, torch_mod, tra)
+
+pytestmark = pytest.mark.gpu
+
+ENT_TOL = 1e-3
+LSE_TOL = 1e-3
+
+
+def _to_gpu_tile_major(t, wl, q, k, v):
+    torch = torch_mod()
+    dev = device()
+    qp = t.tile_major_permute(q.to(dev), wl.F, wl.H, wl.W)
+    kp = t.tile_major_permute(k.to(dev), wl.F, wl.H, wl.W)
+    vp = t.tile_major_permute(v.to(dev), wl.F, wl.H, wl.W)
+    return qp, kp, vp
+
+
+def _np64(x):
+    return x.float().numpy().astype(np.float64)
+
+
+def _check_dense(orc, wl, q, k, v, o, H, L, heads, rows=None):
+    """o, H, L: GPU results (tile-major, CPU numpy).  rows: tile-major positions to check."""
+    perm = orc.tile_major_order(wl.F, wl.H, wl.W)
+    worst = [0.0, 0.0, 0.0]
+    for h in heads:
+        rr = np.arange(wl.N, dtype=np.int32) if rows is None else rows
+        nat = perm[rr].astype(np.int32)
+        ro, rH, rL = orc.attention(_np64(q[h]), _np64(k[h]), _np64(v[h]), wl.sm_scale, rows=nat)
+        err, rl = check_output(o[h][rr], ro, wl.dtype)
+        e_ent = float(np.max(np.abs(H[h][rr] - rH)))
+        e_lse = float(np.max(np.abs(L[h][rr] - rL)))
+        assert e_ent <= ENT_TOL, "head %d entropy err %.3g" % (h, e_ent)
+        assert e_lse <= LSE_TOL, "head %d lse err %.3g" % (h, e_lse)
+        worst = [max(worst[0], err), max(worst[1], e_ent), max(worst[2], e_lse)]
+    say("  max-abs out %.3g, entropy %.3g, lse %.3g" % tuple(worst))
+
+
+def _run_dense(t, wl, q, k, v):
+    torch = torch_mod()
+    qp, kp, vp = _to_gpu_tile_major(t, wl, q, k, v)
+    o, H, L = t.dense_attn_entropy(qp, kp, vp, wl.sm_scale, entropy=True, lse=True)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), H.cpu().numpy(), L.cpu().numpy()
+
+
+def test_dense_tiny_fp32_full(orc):
+    wl = workloads.get(1)
+    t = tra()
+    say("dense tiny fp32 full")
+    q, k, v = qkv_inputs(wl)
+    o, H, L = _run_dense(t, wl, q, k, v)
+    _check_dense(orc, wl, q, k, v, o, H, L, heads=range(wl.outer))
+
+
+@pytest.mark.parametrize("F,H,W,D,dtype", [
+    (3, 15, 17, 128, "bf16"),   # N = 765: ragged q-block and k-block
+    (4, 16, 16, 64, "bf16"),
+    (2, 9, 13, 64, "f32"),      # N = 234
+    (3, 15, 17, 128, "f32"),
+    (1, 1, 1, 128, "bf16"),     # a single token
+    (1, 8, 8, 128, "bf16"),     # exactly one tile
+])
+def test_dense_small_full(orc, F, H, W, D, dtype):
+    wl = small_workload(50 + D, F, H, W, D, dtype)
+    t = tra()
+    say("dense small", F, H, W, D, dtype)
+    q, k, v = qkv_inputs(wl)
+    o, Hh, L = _run_dense(t, wl, q, k, v)
+    _check_dense(orc, wl, q, k, v, o, Hh, L, heads=range(wl.outer))
+
+
+def test_dense_uniform_and_one_hot_closed_forms():
+    # q = 0: every row uniform, H = ln N exactly in theory; one-hot rows: H ~ 0
+    torch = torch_mod()
+    t = tra()
+    dev = device()
+    N, D = 1000, 128
+    q = torch.zeros((1, N, D), dtype=torch.bfloat16, device=dev)
+    k = torch.randn((1, N, D), device=dev).to(torch.bfloat16)
+    v = torch.randn((1, N, D), device=dev).to(torch.bfloat16)
+    o, H, L = t.dense_attn_entropy(q, k, v, entropy=True, lse=True)
+    torch.cuda.synchronize()
+    assert float((H - math.log(N)).abs().max()) < 1e-3
+    assert float((L - math.log(N)).abs().max()) < 1e-3
+    ref = v.float().mean(dim=1, keepdim=True)
+    assert float((o.float() - ref).abs().max()) < 1e-2
+    # one-hot: keys e_j * 64 and queries e_i * 64 (scale 1): logit gap 4096 -> p = delta
+    kk = torch.zeros((1, 128, D), device=dev)
+    kk[0, torch.arange(128), torch.arange(128)] = 64.0
+    o2, H2, _ = t.dense_attn_entropy(kk.to(torch.bfloat16), kk.to(torch.bfloat16),
+                                     torch.eye(128, device=dev)[None].to(torch.bfloat16), sm_scale=1.0)
+    torch.cuda.synchronize()
+    assert float(H2.abs().max()) < 1e-3
+    assert float((o2.float()[0] - torch.eye(128, device=dev)).abs().max()) < 1e-2
+
+
+@pytest.mark.parametrize("wid", [2, 3, 4])
+def test_dense_full_size_sampled(orc, wid):
+    wl = workloads.get(wid)
+    t = tra()
+    say("dense full size workload", wid, wl.name)
+    q, k, v = qkv_inputs(wl)
+    o, H, L = _run_dense(t, wl, q, k, v)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(H))
+    assert np.all(H >= -ENT_TOL) and np.all(H <= math.log(wl.N) + ENT_TOL)
+    _, rows = sample_rows(wid, wl.N, 128, 3)
+    heads = synth.uniform_ints(wid + 10, 2, 0, wl.outer)
+    _check_dense(orc, wl, q, k, v, o, H, L, heads=heads, rows=rows)
+    say("  entropy p10/p50/p90: %.2f %.2f %.2f (ln N %.2f)" % (*np.percentile(H, [10, 50, 90]), math.log(wl.N)))
+
+
+# ------------------------------------------------------------------ block-sparse
+def _lists_from_mask(mask):
+    """mask [outer][nqb][nkb] -> int32 kv_count, kv_index (padded with -7 past the count)."""
+    outer, nqb, nkb = mask.shape
+    cnt = mask.sum(axis=2).astype(np.int32)
+    idx = np.full((outer, nqb, nkb), -7, dtype=np.int32)
+    for o in range(outer):
+        for qb in range(nqb):
+            nz = np.nonzero(mask[o, qb])[0]
+            idx[o, qb, :len(nz)] = nz
+    return cnt, idx
+
+
+def _oracle_masks(orc, ent, wl, heads, qblocks=None):
+    mask = np.zeros((wl.outer, wl.nqb, wl.nkb), dtype=np.uint8)
+    for h in heads:
+        m, _ = orc.block_mask(ent[h], wl.F, wl.H, wl.W, wl.tau, wl.gamma, wl.block_q, wl.block_k,
+                              wl.vote_threshold, qblocks=qblocks)
+        if qblocks is None:
+            mask[h] = m
+        else:
+            mask[h][qblocks] = m
+    return mask
+
+
+def _check_sparse(orc, wl, q, k, v, o, L, mask, heads, rows):
+    perm = orc.tile_major_order(wl.F, wl.H, wl.W)
+    worst = 0.0
+    for h in heads:
+        qp, kp, vp = (orc.permute(_np64(x[h]), perm) for x in (q, k, v))
+        ro, _, rL = orc.attention(qp, kp, vp, wl.sm_scale, rows=rows, block_mask=mask[h], bq=wl.block_q,
+                                  bk=wl.block_k)
+        err, _ = check_output(o[h][rows], ro, wl.dtype)
+        e_lse = float(np.max(np.abs(L[h][rows] - rL)))
+        assert e_lse <= LSE_TOL, "lse err %.3g" % e_lse
+        worst = max(worst, err)
+    say("  sparse max-abs %.3g" % worst)
+
+
+def _run_sparse(t, wl, q, k, v, cnt, idx):
+    torch = torch_mod()
+    dev = device()
+    qp, kp, vp = _to_gpu_tile_major(t, wl, q, k, v)
+    o, L = t.block_sparse_attn(qp, kp, vp, torch.from_numpy(cnt).to(dev), torch.from_numpy(idx).to(dev),
+                               wl.block_q, wl.block_k, wl.sm_scale, lse=True)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), L.cpu().numpy()
+
+
+@pytest.mark.parametrize("F,H,W,D,dtype,bq,tau", [
+    (3, 15, 17, 128, "bf16", 128, 0.03),
+    (3, 15, 17, 128, "bf16", 64, 0.03),
+    (4, 16, 16, 64, "bf16", 64, 0.01),
+    (4, 16, 16, 64, "f32", 64, 1.0),
+    (2, 9, 13, 128, "f32", 128, 0.05),
+    (5, 12, 20, 128, "bf16", 128, 0.002),
+])
+def test_sparse_small_full(orc, F, H, W, D, dtype, bq, tau):
+    wl = small_workload(80 + D + bq, F, H, W, D, dtype, bq=bq, tau=tau)
+    t = tra()
+    say("sparse small", F, H, W, D, dtype, bq, tau)
+    q, k, v = qkv_inputs(wl)
+    ent = synth.entropy_like(F + H + W, wl.outer, wl.N)
+    mask = _oracle_masks(orc, ent, wl, range(wl.outer))
+    cnt, idx = _lists_from_mask(mask)
+    o, L = _run_sparse(t, wl, q, k, v, cnt, idx)
+    _check_sparse(orc, wl, q, k, v, o, L, mask, range(wl.outer), np.arange(wl.N, dtype=np.int32))
+    # cross-step reuse: a new draw of q, k, v with the same mask
+    q2, k2, v2 = qkv_inputs(small_workload(wl.wid + 1, F, H, W, D, dtype, bq=bq, tau=tau))
+    o2, L2 = _run_sparse(t, wl, q2, k2, v2, cnt, idx)
+    _check_sparse(orc, wl, q2, k2, v2, o2, L2, mask, [0], np.arange(wl.N, dtype=np.int32))
+
+
+def test_sparse_all_blocks_equals_dense_bitexact():
+    torch = torch_mod()
+    t = tra()
+    dev = device()
+    for (N, D) in ((2000, 128), (1500, 64)):
+        say("sparse all blocks == dense", N, D)
+        q, k, v = (torch.randn((2, N, D), device=dev).to(torch.bfloat16) for _ in range(3))
+        o_d, _, L_d = t.dense_attn_entropy(q, k, v, entropy=False, lse=True)
+        nqb, nkb = -(-N // 128), -(-N // 64)
+        cnt = torch.full((2, nqb), nkb, dtype=torch.int32, device=dev)
+        idx = torch.arange(nkb, dtype=torch.int32, device=dev).repeat(2, nqb, 1).contiguous()
+        o_s, L_s = t.block_sparse_attn(q, k, v, cnt, idx, 128, 64, lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o_d.view(torch.int16), o_s.view(torch.int16))
+        assert torch.equal(L_d, L_s)
+
+
+def test_sparse_empty_row_and_determinism():
+    torch = torch_mod()
+    t = tra()
+    dev = device()
+    N, D = 700, 128
+    q, k, v = (torch.randn((1, N, D), device=dev).to(torch.bfloat16) for _ in range(3))
+    nqb, nkb = -(-N // 128), -(-N // 64)
+    cnt = torch.full((1, nqb), 3, dtype=torch.int32, device=dev)
+    cnt[0, 2] = 0
+    idx = torch.zeros((1, nqb, nkb), dtype=torch.int32, device=dev)
+    idx[0, :, :3] = torch.tensor([0, 4, nkb - 1], dtype=torch.int32, device=dev)
+    o1, L1 = t.block_sparse_attn(q, k, v, cnt, idx, lse=True)
+    o2, L2 = t.block_sparse_attn(q, k, v, cnt, idx, lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(L1, L2)
+    assert float(o1[0, 256:384].float().abs().max()) == 0.0
+    assert bool(torch.isinf(L1[0, 256:384]).all())
+
+
+@pytest.mark.parametrize("wid", [3, 4, 2, 5])
+def test_sparse_full_size_sampled(orc, wid):
+    # every head and q-block runs on the GPU with a GPU-built mask; the oracle checks seeded
+    # q-blocks of seeded heads against its own mask rows from the same entropy array
+    wl = workloads.get(wid)
+    t = tra()
+    torch = torch_mod()
+    dev = device()
+    say("sparse full size workload", wid, wl.name, "tau", wl.tau)
+    q, k, v = qkv_inputs(wl)
+    if wl.static_mask:
+        ent = np.repeat(synth.entropy_like(500 + wid, wl.outer, 1), wl.N, axis=1)
+    else:
+        ent = synth.entropy_like(300 + wid, wl.outer, wl.N)
+    cnt, idx, _ = t.build_block_mask(torch.from_numpy(ent).to(dev), wl.F, wl.H, wl.W, wl.tau, wl.gamma,
+                                     wl.block_q, wl.block_k, wl.vote_threshold)
+    qp, kp, vp = _to_gpu_tile_major(t, wl, q, k, v)
+    o, L = t.block_sparse_attn(qp, kp, vp, cnt, idx, wl.block_q, wl.block_k, wl.sm_scale, lse=True)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    L = L.cpu().numpy()
+    assert np.all(np.isfinite(o))
+    blocks, rows = sample_rows(wid + 20, wl.N, wl.block_q, 3)
+    heads = synth.uniform_ints(wid + 30, 2, 0, wl.outer)
+    mask = _oracle_masks(orc, ent, wl, heads, qblocks=blocks)
+    _check_sparse(orc, wl, q, k, v, o, L, mask, heads, rows)
