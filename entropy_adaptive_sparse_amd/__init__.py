@@ -49,6 +49,13 @@ def load():
     with _lock:
         if _lib is not None:
             return _lib
+        # torch ships its own HIP runtime (same soname as ROCm's libamdhip64.so.7).  Loading
+        # torch first makes libtra.so bind to that runtime, so the process holds one HIP/HSA
+        # runtime; the other order would load a second runtime that sees no device.
+        try:
+            import torch  # noqa: F401
+        except ImportError:  # pragma: no cover - a plain C caller needs no torch
+            pass
         if not os.path.exists(_LIBPATH):
             raise RuntimeError("libtra.so is not built (%s); run `python -m entropy_adaptive_sparse_amd.build`"
                                % _LIBPATH)

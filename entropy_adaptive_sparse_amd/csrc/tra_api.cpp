@@ -9,6 +9,8 @@
 #include "tra_internal.h"
 
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -21,6 +23,20 @@ namespace {
 using tra::TileGeom;
 
 constexpr int64_t kMaxN = (int64_t)1 << 30;
+
+// Maps a HIP status to TRA_ERR_HIP; with TRA_DEBUG set in the environment the HIP
+// error string goes to stderr.
+tra_status from_hip(hipError_t e, const char *where) {
+    if (e == hipSuccess) return TRA_OK;
+    static const bool debug = std::getenv("TRA_DEBUG") != nullptr;
+    if (debug) std::fprintf(stderr, "tra: %s: %s (%d)\n", where, hipGetErrorString(e), (int)e);
+    return TRA_ERR_HIP;
+}
+
+// The kernels report launch failures through hipGetLastError(); an error left
+// pending by earlier, unrelated runtime calls is cleared first so that it is not
+// reported as ours.
+void clear_pending_error() { (void)hipGetLastError(); }
 
 bool valid_dtype(tra_dtype dt) { return dt == TRA_F32 || dt == TRA_BF16; }
 int64_t dtype_bytes(tra_dtype dt) { return dt == TRA_F32 ? 4 : 2; }
@@ -134,7 +150,8 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 tra_status get_tables(const TileGeom &g, float tau, float gamma, int bk, tra::MaskTables &out) {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return TRA_ERR_HIP;
+    const hipError_t de = hipGetDevice(&dev);
+    if (de != hipSuccess) return from_hip(de, "hipGetDevice");
     const TableKey key{dev, g.F, g.H, g.W, bk, g.th, g.tw, fbits(tau), fbits(gamma)};
     std::lock_guard<std::mutex> lock(g_mu);
     auto it = g_tables.find(key);
@@ -164,10 +181,12 @@ tra_status get_tables(const TileGeom &g, float tau, float gamma, int bk, tra::Ma
     if (!rects.empty())
         std::memcpy(host.data() + b_lam + b_lnT + b_off, rects.data(), rects.size() * sizeof(int4));
     void *mem = nullptr;
-    if (hipMalloc(&mem, host.size()) != hipSuccess) return TRA_ERR_HIP;
-    if (hipMemcpy(mem, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
+    const hipError_t me = hipMalloc(&mem, host.size());
+    if (me != hipSuccess) return from_hip(me, "hipMalloc of mask tables");
+    const hipError_t ce = hipMemcpy(mem, host.data(), host.size(), hipMemcpyHostToDevice);
+    if (ce != hipSuccess) {
         (void)hipFree(mem);
-        return TRA_ERR_HIP;
+        return from_hip(ce, "upload of mask tables");
     }
     TableEntry e;
     e.mem = mem;
@@ -212,7 +231,7 @@ tra_status check_attn_common(const void *q, const void *k, const void *v, const 
     return TRA_OK;
 }
 
-tra_status from_hip(hipError_t e) { return e == hipSuccess ? TRA_OK : TRA_ERR_HIP; }
+
 
 tra_status permute_impl(const void *src, void *dst, int outer, int F, int H, int W, int row_elems, tra_dtype dt,
                         int tile_h, int tile_w, hipStream_t s, int dir) {
@@ -222,7 +241,9 @@ tra_status permute_impl(const void *src, void *dst, int outer, int F, int H, int
     const tra_status st = check_grid(F, H, W, tile_h, tile_w, g);
     if (st != TRA_OK) return st;
     if ((int64_t)outer * g.N > ((int64_t)1 << 40)) return TRA_ERR_UNSUPPORTED;
-    return from_hip(tra::launch_permute(src, dst, outer, g, (int64_t)row_elems * dtype_bytes(dt), dir, s));
+    clear_pending_error();
+    return from_hip(tra::launch_permute(src, dst, outer, g, (int64_t)row_elems * dtype_bytes(dt), dir, s),
+                    "permute");
 }
 
 }  // namespace
@@ -262,7 +283,8 @@ tra_status tra_dense_attn_entropy(const void *q, const void *k, const void *v, v
     a.nkb = (N + 63) / 64;
     a.sm_scale = sm_scale;
     a.c = (float)((double)sm_scale * 1.4426950408889634074);
-    return from_hip(tra::launch_attention(a, D, dt == TRA_BF16 ? 1 : 0, 128, false, s));
+    clear_pending_error();
+    return from_hip(tra::launch_attention(a, D, dt == TRA_BF16 ? 1 : 0, 128, false, s), "dense attention");
 }
 
 tra_status tra_mask_prepare(int F, int H, int W, float tau, float gamma, int block_q, int block_k, int tile_h,
@@ -294,7 +316,8 @@ tra_status tra_build_block_mask(const float *entropy, int outer, int F, int H, i
     a.block_q = block_q; a.block_k = block_k; a.vote = vote_threshold;
     a.g = g;
     a.kv_count = kv_count; a.kv_index = kv_index; a.block_mask = block_mask;
-    return from_hip(tra::launch_build_mask(a, s));
+    clear_pending_error();
+    return from_hip(tra::launch_build_mask(a, s), "build mask");
 }
 
 tra_status tra_block_sparse_attn(const void *q, const void *k, const void *v, void *o, float *lse,
@@ -314,7 +337,8 @@ tra_status tra_block_sparse_attn(const void *q, const void *k, const void *v, vo
     a.nkb = (N + block_k - 1) / block_k;
     a.sm_scale = sm_scale;
     a.c = (float)((double)sm_scale * 1.4426950408889634074);
-    return from_hip(tra::launch_attention(a, D, dt == TRA_BF16 ? 1 : 0, block_q, true, s));
+    clear_pending_error();
+    return from_hip(tra::launch_attention(a, D, dt == TRA_BF16 ? 1 : 0, block_q, true, s), "sparse attention");
 }
 
 }  // extern "C"
