@@ -43,7 +43,22 @@ def parse():
     p.add_argument("--tau", type=float, default=None)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB (3 times), to calibrate HBM counters")
     return p.parse_args()
+
+
+def copy_calibration(mib: int) -> None:
+    """A plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE counters per dispatch
+    should read mib MiB each; the ratio scales the counters of the TRA kernels."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_mib": mib, "bytes_read": n * 4, "bytes_written": n * 4}), flush=True)
 
 
 def retained_pairs(torch, cnt, idx, N, bq, bk):
@@ -96,6 +111,9 @@ def cpu_baseline(wl, q, k, v, mask_rows, blocks, head, budget_s, perm):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested). "
               "Sharding by (batch, head) needs no exchange inside TRA; see the design notes." % args.gpus,

@@ -7,32 +7,24 @@
 // a block-sparse attention backend; the warm-up mask is reused by later steps) and
 // section 3 contribution 3 (entropy fused into the attention kernel).
 //
-// Both modes share one tile engine.  A workgroup owns 32 * NW queries (NW
-// wavefronts, 32 queries each) and walks 64-key tiles: every k-block in order
-// (dense) or the k-blocks listed in kv_index (sparse).  Per tile, per wavefront:
-//   S^T = K Q^T     (keys x queries) on MFMA, K from LDS, Q^T held in registers;
-//   online softmax  in base 2 with a lazily refreshed running max (the max is only
-//                   moved when a tile raises it by more than 2^8, so the O rescale
-//                   is skipped on almost every tile);
-//   entropy         one extra FMA per score: with x = s * sm_scale * log2 e,
-//                   l = sum 2^(x - m), t = sum 2^(x - m) (x - m); a move of the
-//                   max m -> m' maps (l, t) to (a l, a (t + (m - m') l)),
-//                   a = 2^(m - m'); at the end H = ln 2 (log2 l - t / l) nats;
-//   O^T += V^T P^T  on MFMA, V^T from LDS, P^T straight from the S^T registers.
-// The transposed products keep every per-query statistic inside one lane (a lane
-// owns one query and half of the keys of each tile), so only the tile max crosses
-// lanes (one swap between the two lane halves).  K and V^T tiles are double
-// buffered in LDS (one barrier per tile); the next tile's global loads are in
-// flight while the current tile is computed.
-//
-// LDS layouts (16-byte granules, XOR-swizzled so that the MFMA operand reads and
-// the staging writes are bank-conflict free):
-//   K   [64 keys][D]  : 16-byte chunk c of key row r sits at chunk c ^ (r & 7).
-//   V^T [D][64 keys]  : 8-byte chunk c (4 consecutive keys) of dim row n sits at
-//                       chunk perm(c) ^ 2 * ((n ^ (n >> 3)) & 7), where perm swaps
-//                       bits 0 and 1 of c so that the 8 keys one lane feeds to an
-//                       MFMA (keys 4h..4h+3 and 8+4h..8+4h+3 of a 16-key step) are
-//                       one 16-byte read.
+// Both modes share one tile engine (bf16 inputs, fp32 accumulation).  A workgroup owns
+// one q-block; each wavefront owns 32 queries and walks 64-key tiles: every k-block in
+// order (dense) or the k-blocks listed in kv_index (sparse).  Per tile and wavefront:
+//   S^T = K Q^T      on MFMA (v_mfma_f32_32x32x16_bf16), K from LDS, Q^T in registers,
+//                    so a lane owns one query and 32 of the tile's keys;
+//   softmax          in base 2 with a lazily moved running max (it only moves when a
+//                    tile raises it by more than 2^8, so O is rarely rescaled);
+//   entropy          one extra FMA per score: with x = s * sm_scale * log2 e,
+//                    l = sum 2^(x - m), t = sum 2^(x - m) (x - m); moving the max
+//                    m -> m' maps (l, t) to (a l, a (t + (m - m') l)), a = 2^(m - m');
+//                    at the end H = ln 2 (log2 l - t / l) nats;
+//   O^T += V^T P^T   on MFMA, P^T straight from the S^T registers (bf16), the
+//                    exponentials of one 16-key chunk running under the products of the
+//                    previous chunk.
+// Per-query statistics stay inside one lane; the two lanes that share a query combine
+// with one v_permlane32_swap.  K and V tiles are copied global -> LDS directly (no
+// staging registers) into double buffers while the current tile is computed; one
+// barrier per tile.
 #include "tra_internal.h"
 
 #include <hip/hip_bf16.h>
@@ -61,7 +53,32 @@ __device__ inline int xcd_remap(int bid, int total) {
     return x * q + min(x, r) + k;
 }
 
-__device__ inline float wave_swap_halves(float v) { return __shfl_xor(v, 32); }
+// Lane l and lane l ^ 32 hold the two halves of one query's keys.  v_permlane32_swap on two
+// copies of v leaves {v[l], v[l ^ 32]} in the two results of every lane.  The results are
+// copied to scalars before the bit cast: a bit cast applied directly to an element of the
+// returned vector reads element 0 for both (a front-end code generation bug).
+__device__ inline void pair_values(float v, float &a, float &b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    a = __builtin_bit_cast(float, r0);
+    b = __builtin_bit_cast(float, r1);
+#else
+    a = v;
+    b = v;
+#endif
+}
+__device__ inline float pair_max(float v) {
+    float a, b;
+    pair_values(v, a, b);
+    return fmaxf(a, b);
+}
+__device__ inline float pair_sum(float v) {
+    float a, b;
+    pair_values(v, a, b);
+    return a + b;
+}
 
 // ----------------------------------------------------------------------------------
 // softmax / entropy state of one lane (one query, half of each tile's keys)
@@ -79,7 +96,7 @@ __device__ inline void online_softmax(f32x16_t (&s)[2], RowState &st, float c, f
     for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[b][r]);
-    const float mt = fmaxf(mloc, wave_swap_halves(mloc)) * c;
+    const float mt = pair_max(mloc) * c;
     if (__any(mt > st.m + kLazy)) {
         const float mn = fmaxf(st.m, mt);
         const float al = __builtin_amdgcn_exp2f(st.m - mn);
@@ -107,258 +124,354 @@ __device__ inline void online_softmax(f32x16_t (&s)[2], RowState &st, float c, f
     if (ENT) st.t += ts;
 }
 
-template <int D>
-struct Bf16Tile {
-    static constexpr int KROW = D * 2;                // bytes per K row
-    static constexpr int KBYTES = KT * KROW;          // K tile bytes
-    static constexpr int VBYTES = D * KT * 2;         // V^T tile bytes
-    static constexpr int BUF = KBYTES + VBYTES;
-    static constexpr int KCH = D / 8;                 // 16-byte chunks per K row
-    static constexpr int KUNITS = KT * KCH;           // 16-byte K units per tile
-    static constexpr int VUNITS = (KT / 4) * (D / 8); // (4 keys x 8 dims) V units per tile
+// ----------------------------------------------------------------------------------
+// bf16 tile engine
+//
+// LDS holds K and V tiles row-major ([64 keys][D] bf16, no padding) with the 16-byte
+// chunk c of key row r stored at chunk c ^ (r & 7).  Tiles arrive by direct
+// global->LDS loads (each lane's 16 bytes land at base + 16 * lane, so a lane simply
+// fetches the global chunk that belongs in its slot): no staging registers, no VALU.
+//  - K operand of S^T = K Q^T: lane (ql, h) reads key 32 b + ql, chunk 2 ks + h.
+//  - V^T operand of O^T = V^T P^T: two LDS transpose reads (ds_read_b64_tr_b16) per
+//    MFMA.  Within each 16-lane group, output lane j receives element j % 4 of the
+//    4-element rows fetched by source lanes j / 4 + 4 k (k = 0..3); source lane
+//    16 g + i points at key 16 s + 4 h + i / 4 (+ 8 for the second read), dims
+//    32 db + 16 (g % 2) + 4 (i % 4), so lane (ql, h) ends up with dim 32 db + ql of
+//    keys 16 s + 4 h + 0..3 and 16 s + 8 + 4 h + 0..3 -- exactly the keys whose
+//    probabilities it holds in its S^T registers.
+// Every operand read is one of a few per-lane base offsets plus an immediate, and
+// each read instruction hits every LDS bank the minimum number of times.
+// ----------------------------------------------------------------------------------
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+template <int D, int NT>
+struct Bf16Cfg {
+    static constexpr int ROW = D * 2;              // bytes per key row
+    static constexpr int TILE = KT * ROW;          // bytes per K or V tile
+    static constexpr int NCH = D / 8;              // 16-byte chunks per row
+    static constexpr int SLOTS = KT * NCH;         // 16-byte slots per tile
+    static constexpr int DMA = SLOTS / NT;         // slots per thread per tile
+    static constexpr int LDS = 4 * TILE;           // K x2, V x2
+    static_assert(SLOTS % NT == 0, "tile must split evenly over the workgroup");
 };
 
+// direct global -> LDS copy of one tile; src: the tile's first byte; the wavefront's
+// slots are the DMA consecutive 64-slot ranges starting at slot 64 * DMA * wave.
 template <int D, int NT>
-struct Bf16Stage {
-    static constexpr int KL = (Bf16Tile<D>::KUNITS + NT - 1) / NT;
-    static constexpr int VL = (Bf16Tile<D>::VUNITS + NT - 1) / NT;
-    u32x4_t k[KL];
-    u32x4_t v[VL][4];
-};
-
-// global -> registers for one 64-key tile starting at key0 (keys >= N read as zero)
-template <int D, int NT>
-__device__ inline void bf16_load_tile(Bf16Stage<D, NT> &st, const __bf16 *__restrict__ kp,
-                                      const __bf16 *__restrict__ vp, int key0, int N, int tid) {
-    using T = Bf16Tile<D>;
+__device__ inline void dma_tile(const char *__restrict__ src, lds_char_t *dst, const int *soff, int wave) {
+    using C = Bf16Cfg<D, NT>;
 #pragma unroll
-    for (int i = 0; i < Bf16Stage<D, NT>::KL; ++i) {
-        const int u = tid + i * NT;
-        const int r = u / T::KCH, ch = u - r * T::KCH;
-        u32x4_t val = {0u, 0u, 0u, 0u};
-        if (u < T::KUNITS && key0 + r < N)
-            val = *reinterpret_cast<const u32x4_t *>(kp + (int64_t)(key0 + r) * D + ch * 8);
-        st.k[i] = val;
-    }
-#pragma unroll
-    for (int i = 0; i < Bf16Stage<D, NT>::VL; ++i) {
-        const int u = tid + i * NT;
-        const int dg = u % (D / 8), kg = u / (D / 8);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int key = key0 + kg * 4 + j;
-            u32x4_t val = {0u, 0u, 0u, 0u};
-            if (u < T::VUNITS && key < N)
-                val = *reinterpret_cast<const u32x4_t *>(vp + (int64_t)key * D + dg * 8);
-            st.v[i][j] = val;
-        }
-    }
+    for (int i = 0; i < C::DMA; ++i)
+        __builtin_amdgcn_global_load_lds(src + soff[i], dst + (wave * C::DMA + i) * 1024, 16, 0, 0);
 }
 
-__device__ inline int vt_chunk(int c, int n) {
-    const int pc = (c & ~3) | ((c & 1) << 1) | ((c >> 1) & 1);
-    return pc ^ (2 * ((n ^ (n >> 3)) & 7));
-}
-
-// registers -> LDS (K swizzled, V transposed + swizzled)
+// copy the tile of 64 keys starting at key0; rows past N in a ragged last tile are
+// fetched from row N - 1 (finite values; their scores are masked later)
 template <int D, int NT>
-__device__ inline void bf16_store_tile(const Bf16Stage<D, NT> &st, char *buf, int tid) {
-    using T = Bf16Tile<D>;
-    char *ks = buf;
-    char *vs = buf + T::KBYTES;
-#pragma unroll
-    for (int i = 0; i < Bf16Stage<D, NT>::KL; ++i) {
-        const int u = tid + i * NT;
-        if (u < T::KUNITS) {
-            const int r = u / T::KCH, ch = u - r * T::KCH;
-            *reinterpret_cast<u32x4_t *>(ks + r * T::KROW + ((ch ^ (r & 7)) << 4)) = st.k[i];
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < Bf16Stage<D, NT>::VL; ++i) {
-        const int u = tid + i * NT;
-        if (u < T::VUNITS) {
-            const int dg = u % (D / 8), kg = u / (D / 8);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {  // dims 8dg + 2w, 8dg + 2w + 1
-                const unsigned a0 = st.v[i][0][w], a1 = st.v[i][1][w], a2 = st.v[i][2][w], a3 = st.v[i][3][w];
-                // even dim: low halves; odd dim: high halves
-                u32x2_t ev, od;
-                ev[0] = (a0 & 0xffffu) | (a1 << 16);
-                ev[1] = (a2 & 0xffffu) | (a3 << 16);
-                od[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-                od[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-                const int n0 = dg * 8 + 2 * w, n1 = n0 + 1;
-                *reinterpret_cast<u32x2_t *>(vs + n0 * (KT * 2) + (vt_chunk(kg, n0) << 3)) = ev;
-                *reinterpret_cast<u32x2_t *>(vs + n1 * (KT * 2) + (vt_chunk(kg, n1) << 3)) = od;
-            }
-        }
-    }
-}
-
-// ----------------------------------------------------------------------------------
-// bf16 kernel
-// ----------------------------------------------------------------------------------
-template <int D, int NW, bool SPARSE, bool ENT>
-__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_kernel(AttnArgs a) {
-    constexpr int NT = NW * 64;
-    constexpr int BQ = NW * 32;
-    using T = Bf16Tile<D>;
-    __shared__ __attribute__((aligned(16))) char smem[2 * T::BUF];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int h = lane >> 5, ql = lane & 31;
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int o = bid / a.nqb;
-    const int qb = bid - o * a.nqb;
-    const int N = a.N;
-    const int64_t head = (int64_t)o * N * D;
-    const __bf16 *qp = static_cast<const __bf16 *>(a.q) + head;
-    const __bf16 *kp = static_cast<const __bf16 *>(a.k) + head;
-    const __bf16 *vp = static_cast<const __bf16 *>(a.v) + head;
-    const int qi = qb * BQ + wave * 32 + ql;
-
-    // Q^T operand: lane holds query qi, dims 16 ks + 8 h .. + 8
-    bf16x8_t qf[D / 16];
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-        u32x4_t val = {0u, 0u, 0u, 0u};
-        if (qi < N) val = *reinterpret_cast<const u32x4_t *>(qp + (int64_t)qi * D + ks * 16 + h * 8);
-        qf[ks] = __builtin_bit_cast(bf16x8_t, val);
-    }
-
-    int ntiles;
-    const int32_t *list = nullptr;
-    if (SPARSE) {
-        const int64_t row = (int64_t)o * a.nqb + qb;
-        ntiles = min(max(a.kv_count[row], 0), a.nkb);
-        list = a.kv_index + row * a.nkb;
+__device__ inline void fetch_tile(const char *__restrict__ base, int key0, int N, lds_char_t *dst, const int *soff,
+                                  int wave, int lane) {
+    using C = Bf16Cfg<D, NT>;
+    if (key0 + KT <= N) {
+        dma_tile<D, NT>(base + (int64_t)key0 * C::ROW, dst, soff, wave);
     } else {
-        ntiles = a.nkb;
-    }
-    auto tile_kb = [&](int it) -> int {
-        if (SPARSE) {
-            const int kb = list[it];
-            return (kb >= 0 && kb < a.nkb) ? kb : -1;
+        int so[C::DMA];
+#pragma unroll
+        for (int i = 0; i < C::DMA; ++i) {
+            const int sl = (wave * C::DMA + i) * 64 + lane;
+            const int row = sl / C::NCH, p = sl % C::NCH;
+            so[i] = min(row, N - 1 - key0) * C::ROW + ((p ^ (row & 7)) << 4);
         }
-        return it;
+        dma_tile<D, NT>(base + (int64_t)key0 * C::ROW, dst, so, wave);
+    }
+}
+
+// S^T = K Q^T for one 64-key tile and the wavefront's two 32-query blocks: each K operand
+// read from LDS feeds two MFMAs (one per query block).
+template <int D, int NT, int QW>
+__device__ inline void qk_tile(f32x16_t (&s)[2][QW], const lds_char_t *kb, const int (&koff)[4],
+                               const bf16x8_t (&qf)[QW][D / 16]) {
+    using C = Bf16Cfg<D, NT>;
+    const f32x16_t zero = {};
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const bf16x8_t av = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(
+                kb + koff[ks & 3] + 128 * (ks >> 2) + b * 32 * C::ROW);
+#pragma unroll
+            for (int q2 = 0; q2 < QW; ++q2)
+                s[b][q2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[q2][ks], ks == 0 ? zero : s[b][q2], 0, 0, 0);
+        }
+    }
+}
+
+template <int QW>
+__device__ inline void mask_tail(f32x16_t (&s)[2][QW], int key0, int N, int h) {
+    if (key0 + KT > N) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (key0 + b * 32 + 8 * (r >> 2) + 4 * h + (r & 3) >= N) {
+#pragma unroll
+                    for (int q2 = 0; q2 < QW; ++q2) s[b][q2][r] = kMasked;
+                }
+    }
+}
+
+__device__ inline unsigned pack_bf16x2(float lo, float hi) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+__device__ inline void wait_dma() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's global->LDS copies have landed
+}
+
+// scaled max over this lane's 32 scores of query block q2, combined with the other half of
+// the query's keys
+template <int QW>
+__device__ inline float tile_max(const f32x16_t (&s)[2][QW], int q2, float c) {
+    float m = fmaxf(s[0][q2][0], s[1][q2][0]);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, s[b][q2][r]);
+    return pair_max(m) * c;
+}
+
+// A workgroup of NW wavefronts owns 32 * QW * NW consecutive queries (one q-block); each
+// wavefront owns QW 32-query MFMA blocks, so every K and V^T operand it reads from LDS feeds
+// QW MFMAs.
+//
+// Step j (K_j and V_j in LDS, K_{j+1} and V_{j+1} in flight):
+//   a. S^T_j = K_j Q^T                                 (MFMA)
+//   b. tile max; lazy max move (O, l, t rescaled)       (short VALU)
+//   c. P_j = exp2(S_j - m), row sums (VALU) and O^T += V^T_j P^T_j (MFMA) in one basic
+//      block: the exponentials of one 16-key chunk run under the products of the previous
+//      chunk.
+template <int D, int NW, int QW, bool SPARSE, bool ENT>
+struct Bf16Kernel {
+    static constexpr int NT = NW * 64;
+    using C = Bf16Cfg<D, NT>;
+
+    struct Ctx {
+        const char *kp, *vp;
+        const int32_t __attribute__((address_space(4))) *list;
+        int N, nkb, ntiles, wave, lane, h;
+        float c;
+        int koff[4];
+        int voff[2];
+        int soff[C::DMA];
+        bf16x8_t qf[QW][D / 16];
+        f32x16_t oacc[D / 32][QW];
+        RowState st[QW];
     };
 
-    f32x16_t oacc[D / 32];
-#pragma unroll
-    for (int d = 0; d < D / 32; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
-    RowState st{kMasked, 0.f, 0.f};
-    const float c = a.c;
-
-    Bf16Stage<D, NT> stage;
-    if (ntiles > 0) {
-        const int kb0 = tile_kb(0);
-        bf16_load_tile<D, NT>(stage, kp, vp, kb0 >= 0 ? kb0 * KT : N, N, tid);
-        bf16_store_tile<D, NT>(stage, smem, tid);
-        if (ntiles > 1) {
-            const int kb1 = tile_kb(1);
-            bf16_load_tile<D, NT>(stage, kp, vp, kb1 >= 0 ? kb1 * KT : N, N, tid);
-        }
+    static __device__ inline int key0_of(const Ctx &x, int j) {
+        if (SPARSE) return min(max(x.list[j], 0), x.nkb - 1) * KT;
+        return j * KT;
     }
-    __syncthreads();
 
-    for (int it = 0; it < ntiles; ++it) {
-        char *cur = smem + (it & 1) * T::BUF;
-        if (it + 1 < ntiles) bf16_store_tile<D, NT>(stage, smem + ((it + 1) & 1) * T::BUF, tid);
-        if (it + 2 < ntiles) {
-            const int kb2 = tile_kb(it + 2);
-            bf16_load_tile<D, NT>(stage, kp, vp, kb2 >= 0 ? kb2 * KT : N, N, tid);
+    // One tile step.  kc / vc: K_j / V_j (read); kd / vd: buffers receiving K_{j+1} / V_{j+1}.
+    // Buffers are distinct LDS objects fixed at compile time, so the reads never wait for
+    // the copies in flight.
+    static __device__ inline void step(Ctx &x, int j, lds_char_t *kc, lds_char_t *vc, lds_char_t *kd,
+                                       lds_char_t *vd) {
+        if (j + 1 < x.ntiles) {
+            const int kn = key0_of(x, j + 1);
+            fetch_tile<D, NT>(x.kp, kn, x.N, kd, x.soff, x.wave, x.lane);
+            fetch_tile<D, NT>(x.vp, kn, x.N, vd, x.soff, x.wave, x.lane);
         }
-        const int kb = tile_kb(it);
-        if (kb >= 0) {
-            const char *ks = cur;
-            const char *vs = cur + T::KBYTES;
-            // S^T = K Q^T : two 32-key blocks
-            f32x16_t s[2];
+        // a. scores of tile j
+        f32x16_t s[2][QW];
+        qk_tile<D, NT, QW>(s, kc, x.koff, x.qf);
+        // b. max of the tile (keys past N are clamped duplicates of a real key and cannot
+        //    raise it), masking of those keys, lazy max move
+        const float c = x.c;
+        float mt[QW];
+        bool move = false;
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
+        for (int q2 = 0; q2 < QW; ++q2) {
+            mt[q2] = tile_max<QW>(s, q2, c);
+            move |= mt[q2] > x.st[q2].m + kLazy;
+        }
+        mask_tail<QW>(s, key0_of(x, j), x.N, x.h);
+        if (__any(move)) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[b][r] = 0.f;
-                const int key = b * 32 + ql;
+            for (int q2 = 0; q2 < QW; ++q2) {
+                const float mn = fmaxf(x.st[q2].m, mt[q2]);
+                const float al = __builtin_amdgcn_exp2f(x.st[q2].m - mn);
+                if (ENT) x.st[q2].t = x.st[q2].l > 0.f ? al * (x.st[q2].t + (x.st[q2].m - mn) * x.st[q2].l) : 0.f;
+                x.st[q2].l *= al;
+                x.st[q2].m = mn;
 #pragma unroll
-                for (int ks2 = 0; ks2 < D / 16; ++ks2) {
-                    const int ch = 2 * ks2 + h;
-                    const bf16x8_t av =
-                        *reinterpret_cast<const bf16x8_t *>(ks + key * T::KROW + ((ch ^ (key & 7)) << 4));
-                    s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks2], s[b], 0, 0, 0);
-                }
+                for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) x.oacc[d][q2][r] *= al;
             }
-            // keys past N in the ragged last tile
-            const int key0 = kb * KT;
-            if (key0 + KT > N) {
+        }
+        // c. exponentials and products, 16 keys at a time
+        float nm[QW], ls[QW], ts[QW];
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
+        for (int q2 = 0; q2 < QW; ++q2) {
+            nm[q2] = -x.st[q2].m;
+            ls[q2] = 0.f;
+            ts[q2] = 0.f;
+        }
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = key0 + b * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if (key >= N) s[b][r] = kMasked;
-                    }
-            }
-            online_softmax<ENT, D / 32>(s, st, c, oacc);
-            // P^T operand for 16-key step j: this lane's S^T entries 8 (j & 1) .. + 8 of block j >> 1
-            bf16x8_t pf[4];
+        for (int jj = 0; jj < 4; ++jj) {
+            u32x4_t pw[QW];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int q2 = 0; q2 < QW; ++q2) {
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
-                    bf16x2_t pr = __builtin_convertvector(
-                        (float __attribute__((ext_vector_type(2)))){s[j >> 1][8 * (j & 1) + e],
-                                                                     s[j >> 1][8 * (j & 1) + e + 1]},
-                        bf16x2_t);
-                    pf[j][e] = pr[0];
-                    pf[j][e + 1] = pr[1];
-                }
-            // O^T += V^T P^T
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const int n = db * 32 + ql;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int pos = vt_chunk(4 * j + h, n);  // pair (4j + 2h, +1) after the bit swap
-                    const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(vs + n * (KT * 2) + (pos << 3));
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[j], oacc[db], 0, 0, 0);
+                    const int b = jj >> 1, r = 8 * (jj & 1) + e;
+                    const float d0 = fmaf(s[b][q2][r], c, nm[q2]), d1 = fmaf(s[b][q2][r + 1], c, nm[q2]);
+                    const float e0 = __builtin_amdgcn_exp2f(d0), e1 = __builtin_amdgcn_exp2f(d1);
+                    ls[q2] += e0 + e1;
+                    if (ENT) ts[q2] = fmaf(e1, d1, fmaf(e0, d0, ts[q2]));
+                    pw[q2][e >> 1] = pack_bf16x2(e0, e1);
                 }
             }
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const lds_char_t *src = vc + x.voff[db & 1] + 128 * (db >> 1) + 16 * jj * C::ROW;
+                const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)src);
+                const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(src + 8 * C::ROW));
+                const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                for (int q2 = 0; q2 < QW; ++q2)
+                    x.oacc[db][q2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8_t, pw[q2]),
+                                                                          x.oacc[db][q2], 0, 0, 0);
+            }
         }
+#pragma unroll
+        for (int q2 = 0; q2 < QW; ++q2) {
+            x.st[q2].l += ls[q2];
+            if (ENT) x.st[q2].t += ts[q2];
+        }
+        // this step's copies have landed and every wavefront is done reading
+        wait_dma();
         __syncthreads();
     }
 
-    // combine the two lane halves of each query and write out
-    const float l = st.l + wave_swap_halves(st.l);
-    const float t = ENT ? st.t + wave_swap_halves(st.t) : 0.f;
-    if (qi < N) {
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        __bf16 *op = static_cast<__bf16 *>(a.o) + head + (int64_t)qi * D;
+    static __device__ void run(const AttnArgs &a) {
+        constexpr int BQ = NW * 32 * QW;
+        __shared__ __attribute__((aligned(1024))) char k0_raw[C::TILE];
+        __shared__ __attribute__((aligned(1024))) char k1_raw[C::TILE];
+        __shared__ __attribute__((aligned(1024))) char v0_raw[C::TILE];
+        __shared__ __attribute__((aligned(1024))) char v1_raw[C::TILE];
+        lds_char_t *K0 = (lds_char_t *)k0_raw, *K1 = (lds_char_t *)k1_raw;
+        lds_char_t *V0 = (lds_char_t *)v0_raw, *V1 = (lds_char_t *)v1_raw;
+
+        Ctx x;
+        const int tid = threadIdx.x;
+        x.lane = tid & 63;
+        x.wave = tid >> 6;
+        x.h = x.lane >> 5;
+        const int ql = x.lane & 31, h = x.h, lane = x.lane;
+        const int bid = xcd_remap(blockIdx.x, gridDim.x);
+        const int o = bid / a.nqb;
+        const int qb = bid - o * a.nqb;
+        const int N = a.N;
+        x.N = N;
+        x.nkb = a.nkb;
+        x.c = a.c;
+        const int64_t head = (int64_t)o * N * D;
+        const __bf16 *qp = static_cast<const __bf16 *>(a.q) + head;
+        x.kp = reinterpret_cast<const char *>(static_cast<const __bf16 *>(a.k) + head);
+        x.vp = reinterpret_cast<const char *>(static_cast<const __bf16 *>(a.v) + head);
+        const int q0 = qb * BQ + x.wave * 32 * QW + ql;  // query of block 0 (block q2: + 32 q2)
+
+        // Q^T operands: lane holds queries q0 + 32 q2, dims 16 ks + 8 h .. + 8
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int q2 = 0; q2 < QW; ++q2) {
+            const int qi = q0 + 32 * q2;
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                bf16x2_t lo = __builtin_convertvector(
-                    (float __attribute__((ext_vector_type(2)))){oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv},
-                    bf16x2_t);
-                bf16x2_t hi = __builtin_convertvector(
-                    (float __attribute__((ext_vector_type(2)))){oacc[db][4 * r4 + 2] * inv,
-                                                                 oacc[db][4 * r4 + 3] * inv},
-                    bf16x2_t);
-                u32x2_t w;
-                w[0] = __builtin_bit_cast(unsigned, lo);
-                w[1] = __builtin_bit_cast(unsigned, hi);
-                *reinterpret_cast<u32x2_t *>(op + db * 32 + 8 * r4 + 4 * h) = w;
+            for (int ks = 0; ks < D / 16; ++ks) {
+                u32x4_t val = {0u, 0u, 0u, 0u};
+                if (qi < N) val = *reinterpret_cast<const u32x4_t *>(qp + (int64_t)qi * D + ks * 16 + h * 8);
+                x.qf[q2][ks] = __builtin_bit_cast(bf16x8_t, val);
             }
-        if (h == 0) {
-            const int64_t idx = (int64_t)o * N + qi;
-            if (ENT && a.ent) a.ent[idx] = l > 0.f ? kLn2 * (__log2f(l) - t / l) : 0.f;
-            if (a.lse) a.lse[idx] = l > 0.f ? kLn2 * (st.m + __log2f(l)) : -INFINITY;
+        }
+        {
+            const int r7 = ql & 7, xx = r7 >> 1;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) x.koff[q] = ql * C::ROW + 32 * (q ^ xx) + 16 * ((h ^ r7) & 1);
+            const int g = lane >> 4, i = lane & 15, hh = g >> 1;
+            const int y = 2 * (g & 1) + ((i & 3) >> 1);
+            const int base = (4 * hh + (i >> 2)) * C::ROW + (y ^ (i >> 2)) * 16 + (i & 1) * 8;
+            x.voff[0] = base + 64 * hh;
+            x.voff[1] = base + 64 * (hh ^ 1);
+        }
+#pragma unroll
+        for (int i = 0; i < C::DMA; ++i) {
+            const int sl = (x.wave * C::DMA + i) * 64 + lane;
+            const int row = sl / C::NCH, p = sl % C::NCH;
+            x.soff[i] = row * C::ROW + ((p ^ (row & 7)) << 4);
+        }
+
+        if (SPARSE) {
+            const int64_t row = (int64_t)o * a.nqb + qb;
+            x.ntiles = min(max(a.kv_count[row], 0), a.nkb);
+            x.list = (const int32_t __attribute__((address_space(4))) *)(a.kv_index + row * a.nkb);
+        } else {
+            x.ntiles = a.nkb;
+            x.list = nullptr;
+        }
+#pragma unroll
+        for (int q2 = 0; q2 < QW; ++q2) {
+#pragma unroll
+            for (int d = 0; d < D / 32; ++d) x.oacc[d][q2] = f32x16_t{};
+            x.st[q2] = RowState{kMasked, 0.f, 0.f};
+        }
+
+        if (x.ntiles > 0) {
+            const int k0 = key0_of(x, 0);
+            fetch_tile<D, NT>(x.kp, k0, N, K0, x.soff, x.wave, lane);
+            fetch_tile<D, NT>(x.vp, k0, N, V0, x.soff, x.wave, lane);
+            wait_dma();
+            __syncthreads();
+            for (int j = 0; j < x.ntiles; j += 2) {
+                step(x, j, K0, V0, K1, V1);
+                if (j + 1 < x.ntiles) step(x, j + 1, K1, V1, K0, V0);
+            }
+        }
+
+        // combine the two lane halves of each query and write out
+#pragma unroll
+        for (int q2 = 0; q2 < QW; ++q2) {
+            const float l = pair_sum(x.st[q2].l);
+            const float t = ENT ? pair_sum(x.st[q2].t) : 0.f;
+            const int qi = q0 + 32 * q2;
+            if (qi < N) {
+                const float inv = l > 0.f ? 1.f / l : 0.f;
+                __bf16 *op = static_cast<__bf16 *>(a.o) + head + (int64_t)qi * D;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        u32x2_t w;
+                        w[0] = pack_bf16x2(x.oacc[db][q2][4 * r4] * inv, x.oacc[db][q2][4 * r4 + 1] * inv);
+                        w[1] = pack_bf16x2(x.oacc[db][q2][4 * r4 + 2] * inv, x.oacc[db][q2][4 * r4 + 3] * inv);
+                        *reinterpret_cast<u32x2_t *>(op + db * 32 + 8 * r4 + 4 * h) = w;
+                    }
+                if (h == 0) {
+                    const int64_t idx = (int64_t)o * N + qi;
+                    if (ENT && a.ent) a.ent[idx] = l > 0.f ? kLn2 * (__log2f(l) - t / l) : 0.f;
+                    if (a.lse) a.lse[idx] = l > 0.f ? kLn2 * (x.st[q2].m + __log2f(l)) : -INFINITY;
+                }
+            }
         }
     }
+};
+
+template <int D, int NW, int QW, bool SPARSE, bool ENT>
+__global__ __launch_bounds__(NW * 64, QW == 1 ? 2 : 1) void attn_bf16_kernel(AttnArgs a) {
+    Bf16Kernel<D, NW, QW, SPARSE, ENT>::run(a);
 }
 
 // ----------------------------------------------------------------------------------
@@ -457,8 +570,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_f32_kernel(AttnArgs a) {
         }
     }
 
-    const float l = st.l + wave_swap_halves(st.l);
-    const float t = ENT ? st.t + wave_swap_halves(st.t) : 0.f;
+    const float l = pair_sum(st.l);
+    const float t = ENT ? pair_sum(st.t) : 0.f;
     if (qi < N) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
         float *op = static_cast<float *>(a.o) + head + (int64_t)qi * D;
@@ -478,17 +591,25 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_f32_kernel(AttnArgs a) {
     }
 }
 
+#ifndef TRA_BF16_QW
+#define TRA_BF16_QW 1
+#endif
+constexpr int kQW = TRA_BF16_QW;  // 32-query MFMA blocks per wavefront in the bf16 kernels
+
+template <int D, int NW, bool SPARSE, bool ENT>
+hipError_t launch_bf16(const AttnArgs &a, unsigned blocks, hipStream_t s) {
+    attn_bf16_kernel<D, NW, kQW, SPARSE, ENT><<<blocks, NW * 64, 0, s>>>(a);
+    return hipGetLastError();
+}
+
 template <int D, int NW>
 hipError_t launch_d(const AttnArgs &a, int dtype, bool sparse, hipStream_t s) {
     const unsigned blocks = (unsigned)((int64_t)a.outer * a.nqb);
     const bool ent = a.ent != nullptr;
     if (dtype == 1) {
-        if (sparse)
-            attn_bf16_kernel<D, NW, true, false><<<blocks, NW * 64, 0, s>>>(a);
-        else if (ent)
-            attn_bf16_kernel<D, NW, false, true><<<blocks, NW * 64, 0, s>>>(a);
-        else
-            attn_bf16_kernel<D, NW, false, false><<<blocks, NW * 64, 0, s>>>(a);
+        if (sparse) return launch_bf16<D, NW, true, false>(a, blocks, s);
+        if (ent) return launch_bf16<D, NW, false, true>(a, blocks, s);
+        return launch_bf16<D, NW, false, false>(a, blocks, s);
     } else {
         if (sparse)
             attn_f32_kernel<D, NW, true, false><<<blocks, NW * 64, 0, s>>>(a);
@@ -503,6 +624,12 @@ hipError_t launch_d(const AttnArgs &a, int dtype, bool sparse, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs &a, int D, int dtype, int block_q, bool sparse, hipStream_t s) {
+    // bf16: 32 * kQW queries per wavefront; fp32: 32 queries per wavefront
+    if (dtype == 1) {
+        constexpr int w64 = 2 / kQW, w128 = 4 / kQW;
+        if (block_q == 64) return D == 64 ? launch_d<64, w64>(a, dtype, sparse, s) : launch_d<128, w64>(a, dtype, sparse, s);
+        return D == 64 ? launch_d<64, w128>(a, dtype, sparse, s) : launch_d<128, w128>(a, dtype, sparse, s);
+    }
     if (block_q == 64) return D == 64 ? launch_d<64, 2>(a, dtype, sparse, s) : launch_d<128, 2>(a, dtype, sparse, s);
     return D == 64 ? launch_d<64, 4>(a, dtype, sparse, s) : launch_d<128, 4>(a, dtype, sparse, s);
 }
