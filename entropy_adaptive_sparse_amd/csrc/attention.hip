@@ -127,20 +127,23 @@ __device__ inline void online_softmax(f32x16_t (&s)[2], RowState &st, float c, f
 // ----------------------------------------------------------------------------------
 // bf16 tile engine
 //
-// LDS holds K and V tiles row-major ([64 keys][D] bf16, no padding) with the 16-byte
-// chunk c of key row r stored at chunk c ^ (r & 7).  Tiles arrive by direct
-// global->LDS loads (each lane's 16 bytes land at base + 16 * lane, so a lane simply
-// fetches the global chunk that belongs in its slot): no staging registers, no VALU.
+// LDS holds K and V tiles row-major ([64 keys][D] bf16, no padding) in 16-byte chunks; chunk
+// c of key row r is stored at chunk c ^ f(r).  The LDS of gfx950 serves 256 bytes (64 banks)
+// per cycle, i.e. 16 lanes of a 16-byte read, and the swizzles make every operand read touch
+// every 16-byte bank group the minimum number of times:
+//   K (16-byte reads, 16 consecutive keys, same chunk):  f(r) = r & 15        (D = 128)
+//                                                         f(r) = (r >> 1) & 7  (D = 64)
+//   V (transpose reads, 8 rows x 64 contiguous bytes):   f(r) = 4 (r & 3)     (D = 128)
+//                                                         f(r) = 4 ((r >> 1) & 1) (D = 64)
+// Tiles arrive by direct global->LDS copies (each lane's 16 bytes land at base + 16 * lane,
+// so a lane fetches the global chunk that belongs in its slot): no staging registers.
 //  - K operand of S^T = K Q^T: lane (ql, h) reads key 32 b + ql, chunk 2 ks + h.
-//  - V^T operand of O^T = V^T P^T: two LDS transpose reads (ds_read_b64_tr_b16) per
-//    MFMA.  Within each 16-lane group, output lane j receives element j % 4 of the
-//    4-element rows fetched by source lanes j / 4 + 4 k (k = 0..3); source lane
-//    16 g + i points at key 16 s + 4 h + i / 4 (+ 8 for the second read), dims
-//    32 db + 16 (g % 2) + 4 (i % 4), so lane (ql, h) ends up with dim 32 db + ql of
-//    keys 16 s + 4 h + 0..3 and 16 s + 8 + 4 h + 0..3 -- exactly the keys whose
-//    probabilities it holds in its S^T registers.
-// Every operand read is one of a few per-lane base offsets plus an immediate, and
-// each read instruction hits every LDS bank the minimum number of times.
+//  - V^T operand of O^T = V^T P^T: two LDS transpose reads (ds_read_b64_tr_b16) per MFMA.
+//    Within each 16-lane group, output lane j receives element j % 4 of the 4-element rows
+//    fetched by source lanes j / 4 + 4 k (k = 0..3); source lane 16 g + i points at key
+//    16 s + 4 h + i / 4 (+ 8 for the second read), dims 32 db + 16 (g % 2) + 4 (i % 4), so
+//    lane (ql, h) ends up with dim 32 db + ql of keys 16 s + 4 h + 0..3 and 16 s + 8 + 4 h +
+//    0..3 -- exactly the keys whose probabilities it holds in its S^T registers.
 // ----------------------------------------------------------------------------------
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
@@ -155,42 +158,43 @@ struct Bf16Cfg {
     static constexpr int DMA = SLOTS / NT;         // slots per thread per tile
     static constexpr int LDS = 4 * TILE;           // K x2, V x2
     static_assert(SLOTS % NT == 0, "tile must split evenly over the workgroup");
+    static __device__ inline int fK(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+    static __device__ inline int fV(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
 // direct global -> LDS copy of one tile; src: the tile's first byte; the wavefront's
 // slots are the DMA consecutive 64-slot ranges starting at slot 64 * DMA * wave.
-template <int D, int NT>
+template <int NDMA>
 __device__ inline void dma_tile(const char *__restrict__ src, lds_char_t *dst, const int *soff, int wave) {
-    using C = Bf16Cfg<D, NT>;
 #pragma unroll
-    for (int i = 0; i < C::DMA; ++i)
-        __builtin_amdgcn_global_load_lds(src + soff[i], dst + (wave * C::DMA + i) * 1024, 16, 0, 0);
+    for (int i = 0; i < NDMA; ++i)
+        __builtin_amdgcn_global_load_lds(src + soff[i], dst + (wave * NDMA + i) * 1024, 16, 0, 0);
 }
 
 // copy the tile of 64 keys starting at key0; rows past N in a ragged last tile are
 // fetched from row N - 1 (finite values; their scores are masked later)
-template <int D, int NT>
+template <int D, int NT, bool ISV>
 __device__ inline void fetch_tile(const char *__restrict__ base, int key0, int N, lds_char_t *dst, const int *soff,
                                   int wave, int lane) {
     using C = Bf16Cfg<D, NT>;
     if (key0 + KT <= N) {
-        dma_tile<D, NT>(base + (int64_t)key0 * C::ROW, dst, soff, wave);
+        dma_tile<C::DMA>(base + (int64_t)key0 * C::ROW, dst, soff, wave);
     } else {
         int so[C::DMA];
 #pragma unroll
         for (int i = 0; i < C::DMA; ++i) {
             const int sl = (wave * C::DMA + i) * 64 + lane;
             const int row = sl / C::NCH, p = sl % C::NCH;
-            so[i] = min(row, N - 1 - key0) * C::ROW + ((p ^ (row & 7)) << 4);
+            so[i] = min(row, N - 1 - key0) * C::ROW + ((p ^ (ISV ? C::fV(row) : C::fK(row))) << 4);
         }
-        dma_tile<D, NT>(base + (int64_t)key0 * C::ROW, dst, so, wave);
+        dma_tile<C::DMA>(base + (int64_t)key0 * C::ROW, dst, so, wave);
     }
 }
 
 // S^T = K Q^T for one 64-key tile and the wavefront's two 32-query blocks: each K operand
 // read from LDS feeds two MFMAs (one per query block).
 template <int D, int NT, int QW>
-__device__ inline void qk_tile(f32x16_t (&s)[2][QW], const lds_char_t *kb, const int (&koff)[4],
+__device__ inline void qk_tile(f32x16_t (&s)[2][QW], const lds_char_t *kb, const int (&koff)[D / 16],
                                const bf16x8_t (&qf)[QW][D / 16]) {
     using C = Bf16Cfg<D, NT>;
     const f32x16_t zero = {};
@@ -198,8 +202,8 @@ __device__ inline void qk_tile(f32x16_t (&s)[2][QW], const lds_char_t *kb, const
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-            const bf16x8_t av = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(
-                kb + koff[ks & 3] + 128 * (ks >> 2) + b * 32 * C::ROW);
+            const bf16x8_t av =
+                *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(kb + koff[ks] + b * 32 * C::ROW);
 #pragma unroll
             for (int q2 = 0; q2 < QW; ++q2)
                 s[b][q2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[q2][ks], ks == 0 ? zero : s[b][q2], 0, 0, 0);
@@ -246,12 +250,13 @@ __device__ inline float tile_max(const f32x16_t (&s)[2][QW], int q2, float c) {
 // wavefront owns QW 32-query MFMA blocks, so every K and V^T operand it reads from LDS feeds
 // QW MFMAs.
 //
-// Step j (K_j and V_j in LDS, K_{j+1} and V_{j+1} in flight):
-//   a. S^T_j = K_j Q^T                                 (MFMA)
-//   b. tile max; lazy max move (O, l, t rescaled)       (short VALU)
-//   c. P_j = exp2(S_j - m), row sums (VALU) and O^T += V^T_j P^T_j (MFMA) in one basic
-//      block: the exponentials of one 16-key chunk run under the products of the previous
-//      chunk.
+// Step j (scores S_j already in registers, K_{j+1} and V_j in LDS; K_{j+2} and V_{j+1}
+// copied in the background):
+//   a. masking of keys past N (ragged last tile only); lazy max move for tile j
+//   b. one basic block: P_j = exp2(S_j - m) and row sums (VALU), O^T += V^T_j P^T_j and
+//      S^T_{j+1} = K_{j+1} Q^T (MFMA), so the exponentials run under both products
+//   c. the max of tile j+1 (taken before its masking: keys past N are clamped duplicates
+//      of a real key and cannot raise it)
 template <int D, int NW, int QW, bool SPARSE, bool ENT>
 struct Bf16Kernel {
     static constexpr int NT = NW * 64;
@@ -262,12 +267,13 @@ struct Bf16Kernel {
         const int32_t __attribute__((address_space(4))) *list;
         int N, nkb, ntiles, wave, lane, h;
         float c;
-        int koff[4];
-        int voff[2];
-        int soff[C::DMA];
+        int koff[D / 16];
+        int voff[D / 32];
+        int soffK[C::DMA], soffV[C::DMA];
         bf16x8_t qf[QW][D / 16];
         f32x16_t oacc[D / 32][QW];
         RowState st[QW];
+        float mt[QW];  // scaled max of the tile whose scores are current
     };
 
     static __device__ inline int key0_of(const Ctx &x, int j) {
@@ -275,34 +281,24 @@ struct Bf16Kernel {
         return j * KT;
     }
 
-    // One tile step.  kc / vc: K_j / V_j (read); kd / vd: buffers receiving K_{j+1} / V_{j+1}.
-    // Buffers are distinct LDS objects fixed at compile time, so the reads never wait for
-    // the copies in flight.
-    static __device__ inline void step(Ctx &x, int j, lds_char_t *kc, lds_char_t *vc, lds_char_t *kd,
-                                       lds_char_t *vd) {
-        if (j + 1 < x.ntiles) {
-            const int kn = key0_of(x, j + 1);
-            fetch_tile<D, NT>(x.kp, kn, x.N, kd, x.soff, x.wave, x.lane);
-            fetch_tile<D, NT>(x.vp, kn, x.N, vd, x.soff, x.wave, x.lane);
-        }
-        // a. scores of tile j
-        f32x16_t s[2][QW];
-        qk_tile<D, NT, QW>(s, kc, x.koff, x.qf);
-        // b. max of the tile (keys past N are clamped duplicates of a real key and cannot
-        //    raise it), masking of those keys, lazy max move
-        const float c = x.c;
-        float mt[QW];
+    // kn: K_{j+1} (read); kd: buffer receiving K_{j+2}; vc: V_j (read); vd: buffer receiving
+    // V_{j+1}; s: S_j; sn: receives S_{j+1} (computed unconditionally: past the last tile it
+    // is unused).  Buffers are distinct LDS objects fixed at compile time, so the reads never
+    // wait for the copies in flight.
+    static __device__ inline void step(Ctx &x, int j, lds_char_t *kn, lds_char_t *kd, lds_char_t *vc,
+                                       lds_char_t *vd, f32x16_t (&s)[2][QW], f32x16_t (&sn)[2][QW]) {
+        if (j + 2 < x.ntiles) fetch_tile<D, NT, false>(x.kp, key0_of(x, j + 2), x.N, kd, x.soffK, x.wave, x.lane);
+        if (j + 1 < x.ntiles) fetch_tile<D, NT, true>(x.vp, key0_of(x, j + 1), x.N, vd, x.soffV, x.wave, x.lane);
+
+        // a.
+        mask_tail<QW>(s, key0_of(x, j), x.N, x.h);
         bool move = false;
 #pragma unroll
-        for (int q2 = 0; q2 < QW; ++q2) {
-            mt[q2] = tile_max<QW>(s, q2, c);
-            move |= mt[q2] > x.st[q2].m + kLazy;
-        }
-        mask_tail<QW>(s, key0_of(x, j), x.N, x.h);
+        for (int q2 = 0; q2 < QW; ++q2) move |= x.mt[q2] > x.st[q2].m + kLazy;
         if (__any(move)) {
 #pragma unroll
             for (int q2 = 0; q2 < QW; ++q2) {
-                const float mn = fmaxf(x.st[q2].m, mt[q2]);
+                const float mn = fmaxf(x.st[q2].m, x.mt[q2]);
                 const float al = __builtin_amdgcn_exp2f(x.st[q2].m - mn);
                 if (ENT) x.st[q2].t = x.st[q2].l > 0.f ? al * (x.st[q2].t + (x.st[q2].m - mn) * x.st[q2].l) : 0.f;
                 x.st[q2].l *= al;
@@ -313,7 +309,9 @@ struct Bf16Kernel {
                     for (int r = 0; r < 16; ++r) x.oacc[d][q2][r] *= al;
             }
         }
-        // c. exponentials and products, 16 keys at a time
+        // b.
+        const float c = x.c;
+        qk_tile<D, NT, QW>(sn, kn, x.koff, x.qf);
         float nm[QW], ls[QW], ts[QW];
 #pragma unroll
         for (int q2 = 0; q2 < QW; ++q2) {
@@ -338,7 +336,7 @@ struct Bf16Kernel {
             }
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                const lds_char_t *src = vc + x.voff[db & 1] + 128 * (db >> 1) + 16 * jj * C::ROW;
+                const lds_char_t *src = vc + x.voff[db] + 16 * jj * C::ROW;
                 const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)src);
                 const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(src + 8 * C::ROW));
                 const bf16x8_t av = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -352,6 +350,8 @@ struct Bf16Kernel {
         for (int q2 = 0; q2 < QW; ++q2) {
             x.st[q2].l += ls[q2];
             if (ENT) x.st[q2].t += ts[q2];
+            // c.
+            x.mt[q2] = tile_max<QW>(sn, q2, c);
         }
         // this step's copies have landed and every wavefront is done reading
         wait_dma();
@@ -398,20 +398,26 @@ struct Bf16Kernel {
             }
         }
         {
-            const int r7 = ql & 7, xx = r7 >> 1;
+            // K operand: chunk 2 ks + h of key ql (+ 32 b), stored at chunk (2 ks + h) ^ fK(ql)
+            const int xk = C::fK(ql);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) x.koff[q] = ql * C::ROW + 32 * (q ^ xx) + 16 * ((h ^ r7) & 1);
+            for (int ks = 0; ks < D / 16; ++ks)
+                x.koff[ks] = ql * C::ROW + 32 * (ks ^ (xk >> 1)) + 16 * (h ^ (xk & 1));
+            // V^T operand source: key 4 hh + i / 4 (+ 16 s, + 8), dims 32 db + 16 (g % 2) + 4 (i % 4)
             const int g = lane >> 4, i = lane & 15, hh = g >> 1;
-            const int y = 2 * (g & 1) + ((i & 3) >> 1);
-            const int base = (4 * hh + (i >> 2)) * C::ROW + (y ^ (i >> 2)) * 16 + (i & 1) * 8;
-            x.voff[0] = base + 64 * hh;
-            x.voff[1] = base + 64 * (hh ^ 1);
+            const int u = 2 * (g & 1) + ((i & 3) >> 1);
+            const int row = 4 * hh + (i >> 2);
+            const int sel = D == 128 ? (i >> 2) : ((i >> 3) & 1);  // fV(row) / 4
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+                x.voff[db] = row * C::ROW + 64 * (db ^ sel) + 16 * u + 8 * (i & 1);
         }
 #pragma unroll
         for (int i = 0; i < C::DMA; ++i) {
             const int sl = (x.wave * C::DMA + i) * 64 + lane;
             const int row = sl / C::NCH, p = sl % C::NCH;
-            x.soff[i] = row * C::ROW + ((p ^ (row & 7)) << 4);
+            x.soffK[i] = row * C::ROW + ((p ^ C::fK(row)) << 4);
+            x.soffV[i] = row * C::ROW + ((p ^ C::fV(row)) << 4);
         }
 
         if (SPARSE) {
@@ -429,15 +435,21 @@ struct Bf16Kernel {
             x.st[q2] = RowState{kMasked, 0.f, 0.f};
         }
 
+        f32x16_t s0[2][QW], s1[2][QW];
         if (x.ntiles > 0) {
             const int k0 = key0_of(x, 0);
-            fetch_tile<D, NT>(x.kp, k0, N, K0, x.soff, x.wave, lane);
-            fetch_tile<D, NT>(x.vp, k0, N, V0, x.soff, x.wave, lane);
+            fetch_tile<D, NT, false>(x.kp, k0, N, K0, x.soffK, x.wave, lane);
+            fetch_tile<D, NT, true>(x.vp, k0, N, V0, x.soffV, x.wave, lane);
+            if (x.ntiles > 1) fetch_tile<D, NT, false>(x.kp, key0_of(x, 1), N, K1, x.soffK, x.wave, lane);
             wait_dma();
             __syncthreads();
+            qk_tile<D, NT, QW>(s0, K0, x.koff, x.qf);
+#pragma unroll
+            for (int q2 = 0; q2 < QW; ++q2) x.mt[q2] = tile_max<QW>(s0, q2, x.c);
+            __syncthreads();  // every wavefront is done with K_0 before K_2 overwrites it
             for (int j = 0; j < x.ntiles; j += 2) {
-                step(x, j, K0, V0, K1, V1);
-                if (j + 1 < x.ntiles) step(x, j + 1, K1, V1, K0, V0);
+                step(x, j, K1, K0, V0, V1, s0, s1);
+                if (j + 1 < x.ntiles) step(x, j + 1, K0, K1, V1, V0, s1, s0);
             }
         }
 
