@@ -109,14 +109,14 @@ void build_rects(const TileGeom &g, int bk, std::vector<int32_t> &off, std::vect
             bool merged = false;
             for (size_t r = first; r < rects.size(); ++r) {
                 int4 &rc = rects[r];
-                const int ry1 = rc.y >> 16, rx0 = rc.z & 0xffff, rx1 = rc.z >> 16;
+                const int rx0 = rc.y >> 16, ry1 = rc.z & 0xffff, rx1 = rc.z >> 16;
                 if (rc.x == f && ry1 == y - 1 && rx0 == x && rx1 == x1) {
-                    rc.y = (rc.y & 0xffff) | (y << 16);
+                    rc.z = y | (x1 << 16);
                     merged = true;
                     break;
                 }
             }
-            if (!merged) rects.push_back(make_int4(f, y | (y << 16), x | (x1 << 16), 0));
+            if (!merged) rects.push_back(make_int4(f, y | (x << 16), y | (x1 << 16), 0));
             p = q;
         }
     }
@@ -170,16 +170,29 @@ tra_status get_tables(const TileGeom &g, float tau, float gamma, int bk, tra::Ma
     } catch (const std::bad_alloc &) {
         return TRA_ERR_CAPACITY;
     }
+    // fixed stride: rmax rectangle slots per k-block, unused slots marked with frame -1
+    const size_t nkb = off.size() - 1;
+    int rmax = 1;
+    for (size_t kb = 0; kb < nkb; ++kb) rmax = std::max(rmax, off[kb + 1] - off[kb]);
+    std::vector<int4> slots;
+    try {
+        slots.assign(nkb * (size_t)rmax, make_int4(-1, 0, 0, -1));
+    } catch (const std::bad_alloc &) {
+        return TRA_ERR_CAPACITY;
+    }
+    for (size_t kb = 0; kb < nkb; ++kb)
+        for (int r = off[kb]; r < off[kb + 1]; ++r) {
+            int4 rc = rects[(size_t)r];
+            rc.w = rc.x;  // a used slot: w = f >= 0
+            slots[kb * (size_t)rmax + (size_t)(r - off[kb])] = rc;
+        }
     const size_t b_lam = align256(lam.size() * sizeof(double));
     const size_t b_lnT = align256(lnT.size() * sizeof(double));
-    const size_t b_off = align256(off.size() * sizeof(int32_t));
-    const size_t b_rect = align256(std::max<size_t>(1, rects.size()) * sizeof(int4));
-    std::vector<char> host(b_lam + b_lnT + b_off + b_rect, 0);
+    const size_t b_rect = align256(slots.size() * sizeof(int4));
+    std::vector<char> host(b_lam + b_lnT + b_rect, 0);
     std::memcpy(host.data(), lam.data(), lam.size() * sizeof(double));
     std::memcpy(host.data() + b_lam, lnT.data(), lnT.size() * sizeof(double));
-    std::memcpy(host.data() + b_lam + b_lnT, off.data(), off.size() * sizeof(int32_t));
-    if (!rects.empty())
-        std::memcpy(host.data() + b_lam + b_lnT + b_off, rects.data(), rects.size() * sizeof(int4));
+    std::memcpy(host.data() + b_lam + b_lnT, slots.data(), slots.size() * sizeof(int4));
     void *mem = nullptr;
     const hipError_t me = hipMalloc(&mem, host.size());
     if (me != hipSuccess) return from_hip(me, "hipMalloc of mask tables");
@@ -193,9 +206,10 @@ tra_status get_tables(const TileGeom &g, float tau, float gamma, int bk, tra::Ma
     char *base = static_cast<char *>(mem);
     e.t.lam = reinterpret_cast<const double *>(base);
     e.t.lnT = reinterpret_cast<const double *>(base + b_lam);
-    e.t.rect_off = reinterpret_cast<const int32_t *>(base + b_lam + b_lnT);
-    e.t.rects = reinterpret_cast<const int4 *>(base + b_lam + b_lnT + b_off);
+    e.t.rects = reinterpret_cast<const int4 *>(base + b_lam + b_lnT);
     e.t.tmax = tmax;
+    e.t.lnTmax = lnT[(size_t)tmax];
+    e.t.rmax = rmax;
     g_tables.emplace(key, e);
     out = e.t;
     return TRA_OK;
@@ -212,8 +226,8 @@ tra_status check_mask_args(int F, int H, int W, float tau, float gamma, int bloc
     if (H > 32767 || W > 32767) return TRA_ERR_UNSUPPORTED;  // rectangle bounds are packed in 16 bits
     const int64_t tmax = (int64_t)(H - 1) * (H - 1) + (int64_t)(W - 1) * (W - 1);
     if (tmax > (int64_t)1 << 28) return TRA_ERR_UNSUPPORTED;
-    const int nkb = (g.N + block_k - 1) / block_k;
-    if (tra::mask_lds_bytes(block_q, F, nkb) > 65536) return TRA_ERR_UNSUPPORTED;
+    if (F > 32767) return TRA_ERR_UNSUPPORTED;  // frame index packed in 16 bits of a list entry
+    if (tra::mask_lds_bytes(block_q, F, g.HW) > 65536) return TRA_ERR_UNSUPPORTED;
     return TRA_OK;
 }
 
@@ -314,6 +328,8 @@ tra_status tra_build_block_mask(const float *entropy, int outer, int F, int H, i
     a.ent = entropy;
     a.outer = outer; a.nqb = nqb; a.nkb = nkb;
     a.block_q = block_q; a.block_k = block_k; a.vote = vote_threshold;
+    a.nqf_max = tra::mask_frames_per_qblock(block_q, g.HW, F);
+    a.chunk = std::min(256, tra::kMaskEntryCap / std::max(1, a.t.rmax));
     a.g = g;
     a.kv_count = kv_count; a.kv_index = kv_index; a.block_mask = block_mask;
     clear_pending_error();

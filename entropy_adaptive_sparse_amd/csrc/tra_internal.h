@@ -50,14 +50,21 @@ hipError_t launch_permute(const void *src, void *dst, int outer, const TileGeom 
 struct MaskTables {
     const double *lam;      // [F][F]  (ln tau - (2 gamma)|f - f'|) - ln(pi S_f)
     const double *lnT;      // [tmax + 1], lnT[t] = ln t, lnT[0] = -inf
-    const int32_t *rect_off;// [nkb + 1]
-    const int4 *rects;      // {f, y0 | y1 << 16, x0 | x1 << 16, 0}, inclusive bounds
+    const int4 *rects;      // [nkb][rmax] {f, y0 | x0 << 16, y1 | x1 << 16, f}: inclusive corners packed
+                            // (row | col << 16); unused slots have x = w = -1
+    double lnTmax;          // lnT[tmax]
     int tmax;               // (H-1)^2 + (W-1)^2
+    int rmax;               // most rectangles in one k-block
 };
+
+// Rectangles the mask kernel can hold in LDS for its exact test per chunk of k-blocks.
+constexpr int kMaskEntryCap = 768;
 
 struct MaskArgs {
     const float *ent;
     int outer, nqb, nkb, block_q, block_k, vote;
+    int nqf_max;      // most frames one q-block touches
+    int chunk;        // k-blocks per chunk: min(256, kMaskEntryCap / rmax)
     TileGeom g;
     MaskTables t;
     int32_t *kv_count;
@@ -66,7 +73,8 @@ struct MaskArgs {
 };
 
 hipError_t launch_build_mask(const MaskArgs &a, hipStream_t s);
-size_t mask_lds_bytes(int block_q, int F, int nkb);
+int mask_frames_per_qblock(int block_q, int HW, int F);
+size_t mask_lds_bytes(int block_q, int F, int HW);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {

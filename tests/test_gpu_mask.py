@@ -42,6 +42,11 @@ def _compare(orc, ent, cnt, idx, msk, F, H, W, tau, gamma, bq, bk, vote, heads, 
     (3, 15, 17, 0.02, 0.0, 128, 1),    # ragged blocks and tiles, no temporal decay
     (5, 9, 22, 0.2, 1.5, 64, 3),
     (2, 45, 80, 0.03, 0.5, 128, 1),    # two frames of the 720p grid
+    (12, 5, 7, 0.05, 0.3, 128, 1),     # frames smaller than a q-block: up to five frames per q-block
+    (12, 5, 7, 0.05, 0.3, 64, 2),
+    (7, 11, 3, 0.5, 0.2, 128, 1),      # columns narrower than a tile
+    (40, 2, 3, 0.3, 0.1, 128, 1),      # 6-token frames: a k-block spans a dozen frames
+    (9, 13, 11, 0.05, 0.4, 64, 2),
 ])
 def test_mask_small_all_blocks(orc, F, H, W, tau, gamma, bq, vote):
     t = tra()
@@ -50,6 +55,30 @@ def test_mask_small_all_blocks(orc, F, H, W, tau, gamma, bq, vote):
     ent = synth.entropy_like(F * 7 + H, 2, N)
     cnt, idx, msk = _gpu_mask(t, ent, F, H, W, tau, gamma, bq, 64, vote)
     _compare(orc, ent, cnt, idx, msk, F, H, W, tau, gamma, bq, 64, vote, heads=range(2))
+
+
+@pytest.mark.parametrize("bq,vote", [(128, 1), (64, 1), (128, 3)])
+def test_mask_special_entropies(orc, bq, vote):
+    # NaN and -inf reach only distance 0, +inf the whole frame; negative, zero and
+    # large finite entropies mixed in, whole frames of NaN included
+    F, H, W = 4, 24, 40
+    N = F * H * W
+    say("mask special entropies", bq, vote)
+    ent = synth.entropy_like(55, 2, N)
+    rng = np.random.default_rng(56)
+    pick = rng.random(ent.shape)
+    ent[pick < 0.05] = np.nan
+    ent[(pick >= 0.05) & (pick < 0.07)] = -np.inf
+    ent[(pick >= 0.075) & (pick < 0.15)] *= -1.0
+    ent[(pick >= 0.15) & (pick < 0.2)] = 0.0
+    ent[(pick >= 0.2) & (pick < 0.205)] = 9.5
+    ent[1, 2 * H * W:3 * H * W] = np.nan
+    ent[0, 17] = np.inf
+    ent[1, 700] = np.inf
+    t = tra()
+    for tau in (0.02, 0.002):
+        cnt, idx, msk = _gpu_mask(t, ent, F, H, W, tau, 0.5, bq, 64, vote)
+        _compare(orc, ent, cnt, idx, msk, F, H, W, tau, 0.5, bq, 64, vote, heads=range(2))
 
 
 def test_mask_from_oracle_entropies_tiny(orc):
