@@ -44,13 +44,19 @@ constexpr float kMasked = -1.0e30f; // score of a key past N (finite: 0 * it sta
 constexpr float kLazy = 8.0f;       // max moves only when it grows by more than this (log2 units)
 constexpr float kLn2 = 0.69314718055994530942f;
 
-// workgroup id -> logical (head, q-block) id such that each XCD (workgroups are
-// dispatched round-robin over 8) receives one contiguous range of logical ids, so
-// neighbouring q-blocks -- which read mostly the same k-blocks -- share an L2.
+// workgroup id -> logical (head, q-block) id.  Workgroups are dispatched round-robin
+// over the 8 XCDs; XCD x receives chunks of kXcdChunk consecutive logical ids (about
+// the q-blocks it runs at once, so neighbouring q-blocks -- which read mostly the same
+// k-blocks -- share its L2), and the chunks of the 8 XCDs advance together through the
+// (head, q-block) order, so all XCDs stay in the same one or two heads and those heads'
+// K and V stay within the last-level cache.  The ragged last row of chunks keeps the
+// identity map (every id still appears exactly once).
+constexpr int kXcdChunk = 32;
 __device__ inline int xcd_remap(int bid, int total) {
-    const int q = total >> 3, r = total & 7;
+    const int full = (total / (8 * kXcdChunk)) * (8 * kXcdChunk);
+    if (bid >= full) return bid;
     const int x = bid & 7, k = bid >> 3;
-    return x * q + min(x, r) + k;
+    return (k / kXcdChunk) * (8 * kXcdChunk) + x * kXcdChunk + (k % kXcdChunk);
 }
 
 // Lane l and lane l ^ 32 hold the two halves of one query's keys.  v_permlane32_swap on two

@@ -6,7 +6,8 @@ Generation", section 3 contribution 4 and section 4); the activations are
 synthetic (``synth.py``).  tau values for workloads 2-4 are calibrated to the
 stated block density (retained token pairs / all token pairs) by
 ``tests/golden/calibrate_tau.py`` with the CPU oracle on a seeded sample of
-q-blocks, then frozen here.
+q-blocks (``tests/golden/tau_calibration.json``), then frozen here; so is the single
+entropy value of the static-mask workload, bisected to the density of workload 3.
 """
 from __future__ import annotations
 
@@ -35,7 +36,8 @@ class Workload:
     t_lo: float = 0.25
     t_hi: float = 8.0
     density_target: float | None = None
-    static_mask: bool = False   # one entropy constant per head instead of per-query entropies
+    static_mask: bool = False   # one entropy value for every query instead of per-query entropies
+    static_entropy: float = 0.0 # that value (nats)
 
     @property
     def outer(self) -> int:
@@ -64,14 +66,14 @@ class Workload:
 
 WORKLOADS = {
     1: Workload(1, "tiny-4x16x16", 1, 2, 64, "f32", 4, 16, 16, 64, 64, tau=1.0),
-    2: Workload(2, "wan2.1-1.3b-480p-21x30x52", 1, 12, 128, "bf16", 21, 30, 52, 128, 64, tau=1.0e-3,
+    2: Workload(2, "wan2.1-1.3b-480p-21x30x52", 1, 12, 128, "bf16", 21, 30, 52, 128, 64, tau=1.23e-3,
                 density_target=0.15),
-    3: Workload(3, "wan2.1-14b-720p-21x45x80", 1, 40, 128, "bf16", 21, 45, 80, 128, 64, tau=3.0e-2,
+    3: Workload(3, "wan2.1-14b-720p-21x45x80", 1, 40, 128, "bf16", 21, 45, 80, 128, 64, tau=3.01e-2,
                 density_target=0.15),
-    4: Workload(4, "hunyuanvideo-13b-720p-33x45x80", 1, 24, 128, "bf16", 33, 45, 80, 128, 64, tau=3.0e-2,
+    4: Workload(4, "hunyuanvideo-13b-720p-33x45x80", 1, 24, 128, "bf16", 33, 45, 80, 128, 64, tau=4.41e-2,
                 t_lo=0.1, t_hi=16.0, density_target=0.15),
-    5: Workload(5, "static-radial-21x45x80", 1, 40, 128, "bf16", 21, 45, 80, 128, 64, tau=3.0e-2,
-                density_target=0.15, static_mask=True),
+    5: Workload(5, "static-radial-21x45x80", 1, 40, 128, "bf16", 21, 45, 80, 128, 64, tau=3.01e-2,
+                density_target=0.15, static_mask=True, static_entropy=10.99),
 }
 
 

@@ -1,0 +1,126 @@
+"""Calibrate tau of the synthetic workloads, and the entropy constant of the static-mask
+workload, with the CPU oracle only.  Writes tests/golden/tau_calibration.json.
+
+Block density = retained (query, key) token pairs / all pairs, the "retained interactions"
+of "Token Radius Attention for Efficient Video Generation" section 4 (the 9-19% range it
+reports).  For each workload with a density target:
+  - seeded heads and q-blocks are sampled; their queries' entropies are the oracle's fp64
+    dense-attention entropies of the seeded bf16-rounded q, k, v (tile-major order), rounded
+    to fp32 -- what the GPU pipeline feeds its mask builder;
+  - log tau is bisected (a fixed 30 steps) until the oracle's block mask of the sampled
+    q-blocks has the target density.
+The static-mask workload (one entropy value for every query, a radial-style mask) bisects
+that value until the density equals the density its base workload reaches at its tau.
+
+Run from the repository root:  python tests/golden/calibrate_tau.py
+The values are then frozen in entropy_adaptive_sparse_amd/workloads.py.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+from entropy_adaptive_sparse_amd import synth, workloads  # noqa: E402
+
+HEADS = 2
+QBLOCKS = 12
+STEPS = 30
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """fp32 -> nearest bf16 (ties to even), returned as fp32."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = ((u >> 16) & 1) + np.uint32(0x7FFF)
+    return ((u + r) & np.uint32(0xFFFF0000)).view(np.float32)
+
+
+def sampled_entropies(wl):
+    """(list of (tile-major entropy vector, q-block sample)) for the sampled heads."""
+    perm = oracle.tile_major_order(wl.F, wl.H, wl.W, wl.tile_h, wl.tile_w)
+    heads = synth.uniform_ints(500 + wl.wid, HEADS, 0, wl.outer)
+    q, k, v = synth.qkv(wl.wid, wl.outer, wl.F, wl.H, wl.W, wl.D, wl.t_lo, wl.t_hi, heads=heads)
+    out = []
+    for s, h in enumerate(heads):
+        qt, kt, vt = (oracle.permute(bf16_round(x[s]).astype(np.float64), perm) for x in (q, k, v))
+        blocks = synth.uniform_ints(600 + 10 * wl.wid + s, QBLOCKS, 0, wl.nqb)
+        rows = np.concatenate([np.arange(b * wl.block_q, min(wl.N, (b + 1) * wl.block_q)) for b in blocks])
+        _, ent, _ = oracle.attention(qt, kt, vt, wl.sm_scale, rows=rows.astype(np.int32))
+        full = np.zeros(wl.N, dtype=np.float32)
+        full[rows] = ent.astype(np.float32)
+        out.append((full, blocks))
+    return out
+
+
+def density(wl, samples, tau: float) -> float:
+    ksz = np.array([min(wl.N, (kb + 1) * wl.block_k) - kb * wl.block_k for kb in range(wl.nkb)], dtype=np.float64)
+    kept = total = 0.0
+    for ent, blocks in samples:
+        mask, _ = oracle.block_mask(ent, wl.F, wl.H, wl.W, tau, wl.gamma, wl.block_q, wl.block_k,
+                                    wl.vote_threshold, wl.tile_h, wl.tile_w, qblocks=blocks)
+        for s, b in enumerate(blocks):
+            nq = min(wl.N, (b + 1) * wl.block_q) - b * wl.block_q
+            kept += nq * float((ksz * mask[s]).sum())
+            total += nq * float(wl.N)
+    return kept / total
+
+
+def bisect(f, lo: float, hi: float, target: float, increasing: bool = True):
+    for _ in range(STEPS):
+        mid = 0.5 * (lo + hi)
+        above = f(mid) > target
+        if above == increasing:
+            hi = mid
+        else:
+            lo = mid
+    return 0.5 * (lo + hi)
+
+
+def main():
+    oracle.build(force=False)
+    result = {"steps": STEPS, "heads_per_workload": HEADS, "qblocks_per_head": QBLOCKS, "workloads": {}}
+    cache = {}
+    for wid in (2, 3, 4):
+        wl = workloads.get(wid)
+        t0 = time.time()
+        samples = sampled_entropies(wl)
+        cache[wid] = samples
+        log_tau = bisect(lambda lt: density(wl, samples, math.exp(lt)), math.log(1e-6), math.log(10.0),
+                         wl.density_target)
+        tau = float("%.3g" % math.exp(log_tau))
+        d = density(wl, samples, tau)
+        result["workloads"][wl.name] = {"tau": tau, "tau_exact": math.exp(log_tau), "density": d,
+                                        "target": wl.density_target, "seconds": round(time.time() - t0, 1)}
+        print(wl.name, result["workloads"][wl.name], flush=True)
+    # static-mask workload: one entropy value for every query of its base workload's samples
+    wl5 = workloads.get(5)
+    base = workloads.get(3)
+    samples = cache[3]
+    base_tau = result["workloads"][base.name]["tau"]
+    target = density(base, samples, base_tau)
+
+    def dens_c(c):
+        flat = [(np.full(base.N, c, dtype=np.float32), blocks) for _, blocks in samples]
+        return density(wl5, flat, base_tau)
+
+    c = bisect(dens_c, 0.0, math.log(base.N), target)
+    c = float("%.4g" % c)
+    result["workloads"][wl5.name] = {"tau": base_tau, "static_entropy": c, "density": dens_c(c),
+                                     "target": target}
+    print(wl5.name, result["workloads"][wl5.name], flush=True)
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tau_calibration.json")
+    with open(path, "w") as fh:
+        json.dump(result, fh, indent=2)
+    print("wrote", path)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,26 @@
+"""The frozen workload parameters agree with the oracle calibration that produced them
+(tests/golden/calibrate_tau.py -> tests/golden/tau_calibration.json)."""
+import json
+import os
+
+from entropy_adaptive_sparse_amd import workloads
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "tau_calibration.json")
+
+
+def test_frozen_tau_matches_calibration():
+    cal = json.load(open(GOLDEN))["workloads"]
+    for wid in (2, 3, 4):
+        wl = workloads.get(wid)
+        c = cal[wl.name]
+        assert wl.tau == c["tau"], wl.name
+        assert abs(c["density"] - wl.density_target) < 0.005, wl.name
+
+
+def test_static_mask_workload_matches_calibration():
+    cal = json.load(open(GOLDEN))["workloads"]
+    wl = workloads.get(5)
+    c = cal[wl.name]
+    assert wl.static_mask and wl.static_entropy == c["static_entropy"] and wl.tau == c["tau"]
+    assert abs(c["density"] - c["target"]) < 0.005
+    assert wl.tau == workloads.get(3).tau
