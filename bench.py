@@ -217,6 +217,20 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     ms_dense_plain = e0.elapsed_time(e1) / 2
+    # the warm-up pass with the mask builder fused in (same outputs as dense_entropy + build_mask)
+    ms_fused = None
+    if wl.dtype == "bf16" and wl.D == 128 and wl.block_q == 128 and not wl.static_mask:
+        def fused():
+            tra.dense_attn_entropy_mask(qp, kp, vp, wl.F, wl.H, wl.W, tau, wl.gamma, wl.sm_scale, wl.block_q,
+                                        wl.block_k, wl.vote_threshold, out=od, ent_out=ent, kv_count=cnt,
+                                        kv_index=idx)
+        fused()
+        e0.record()
+        for _ in range(2):
+            fused()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_fused = e0.elapsed_time(e1) / 2
 
     pairs = retained_pairs(torch, cnt, idx, wl.N, wl.block_q, wl.block_k)
     density = pairs / (wl.outer * float(wl.N) ** 2)
@@ -254,6 +268,8 @@ def main():
         },
         "ms_per_call": {k2: round(v2, 4) for k2, v2 in ms.items()},
         "ms_dense_no_entropy": round(ms_dense_plain, 4),
+        "ms_warmup_separate": round(ms["dense_entropy"] + ms["build_mask"], 4),
+        "ms_warmup_fused": None if ms_fused is None else round(ms_fused, 4),
         "ms_reuse_step": round(ms["permute_qkv"] + ms["sparse_attn"] + ms["unpermute"], 4),
         "roofline": {
             "bound": "mfma", "achieved": round(sparse_tf, 2), "peak": peak, "unit": "TFLOP/s",

@@ -10,6 +10,7 @@ call raises.
 Functions (names as in the C ABI, without the ``tra_`` prefix):
     tile_major_permute / tile_major_unpermute
     dense_attn_entropy
+    dense_attn_entropy_mask (the warm-up pass with the mask builder fused in)
     build_block_mask, mask_prepare
     block_sparse_attn
 """
@@ -21,7 +22,7 @@ import threading
 
 __all__ = [
     "TraError", "library_path", "load", "tile_major_permute", "tile_major_unpermute", "dense_attn_entropy",
-    "build_block_mask", "mask_prepare", "block_sparse_attn", "exported_symbols",
+    "dense_attn_entropy_mask", "build_block_mask", "mask_prepare", "block_sparse_attn", "exported_symbols",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,8 +72,11 @@ def load():
                                              P, P]
         lib.tra_mask_prepare.argtypes = [i32, i32, i32, f32, f32, i32, i32, i32, i32]
         lib.tra_block_sparse_attn.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, f32, i32, i32, P]
+        lib.tra_dense_attn_entropy_mask.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f32, f32, f32,
+                                                    i32, i32, i32, i32, i32, P, P, i64, P, P]
         for name in ("tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
-                     "tra_build_block_mask", "tra_mask_prepare", "tra_block_sparse_attn"):
+                     "tra_build_block_mask", "tra_mask_prepare", "tra_block_sparse_attn",
+                     "tra_dense_attn_entropy_mask"):
             getattr(lib, name).restype = i32
         _lib = lib
         return lib
@@ -80,7 +84,7 @@ def load():
 
 def exported_symbols():
     return ["tra_status_string", "tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
-            "tra_build_block_mask", "tra_mask_prepare", "tra_block_sparse_attn"]
+            "tra_build_block_mask", "tra_mask_prepare", "tra_block_sparse_attn", "tra_dense_attn_entropy_mask"]
 
 
 # ------------------------------------------------------------------------------------------------
@@ -175,6 +179,37 @@ def dense_attn_entropy(q, k, v, sm_scale: float | None = None, entropy: bool = T
     _call("tra_dense_attn_entropy", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(H), _ptr(L), outer, N, D, _dt(q),
           scale, _stream(q))
     return o, H, L
+
+
+def dense_attn_entropy_mask(q, k, v, F: int, H: int, W: int, tau: float, gamma: float, sm_scale: float | None = None,
+                            block_q: int = 128, block_k: int = 64, vote_threshold: int = 1, tile_h: int = 8,
+                            tile_w: int = 8, entropy: bool = True, lse: bool = False, want_mask: bool = False,
+                            out=None, ent_out=None, lse_out=None, kv_count=None, kv_index=None, block_mask=None):
+    """Warm-up pass with the mask fused in.  Returns (o, H, lse, kv_count, kv_index, mask); H, lse and
+    mask are None unless requested (the mask is built from the entropies either way)."""
+    torch = _torch()
+    outer, N, D = _check_qkv(q, k, v)
+    if N != F * H * W:
+        raise ValueError("N must equal F*H*W")
+    dev = q.device
+    o = torch.empty_like(q) if out is None else _dev(out, "out")
+    Hh = None
+    if entropy:
+        Hh = torch.empty((outer, N), dtype=torch.float32, device=dev) if ent_out is None else ent_out
+    L = None
+    if lse:
+        L = torch.empty((outer, N), dtype=torch.float32, device=dev) if lse_out is None else lse_out
+    nqb, nkb = -(-N // block_q), -(-N // block_k)
+    cnt = torch.empty((outer, nqb), dtype=torch.int32, device=dev) if kv_count is None else kv_count
+    idx = torch.empty((outer, nqb, nkb), dtype=torch.int32, device=dev) if kv_index is None else kv_index
+    msk = block_mask
+    if want_mask and msk is None:
+        msk = torch.empty((outer, nqb, nkb), dtype=torch.uint8, device=dev)
+    scale = (1.0 / D ** 0.5) if sm_scale is None else float(sm_scale)
+    _call("tra_dense_attn_entropy_mask", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(Hh), _ptr(L), outer, F, H, W, D,
+          _dt(q), scale, float(tau), float(gamma), block_q, block_k, int(vote_threshold), tile_h, tile_w, _ptr(cnt),
+          _ptr(idx), idx.numel(), _ptr(msk), _stream(q))
+    return o, Hh, L, cnt, idx, msk
 
 
 def mask_prepare(F, H, W, tau, gamma, block_q=128, block_k=64, tile_h=8, tile_w=8) -> None:

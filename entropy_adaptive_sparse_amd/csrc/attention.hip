@@ -25,6 +25,7 @@
 // with one v_permlane32_swap.  K and V tiles are copied global -> LDS directly (no
 // staging registers) into double buffers while the current tile is computed; one
 // barrier per tile.
+#include "mask_impl.h"
 #include "tra_internal.h"
 
 #include <hip/hip_bf16.h>
@@ -364,7 +365,16 @@ struct Bf16Kernel {
         __syncthreads();
     }
 
-    static __device__ void run(const AttnArgs &a) {
+    // Epi: called once the outputs are written, with the four (now free) LDS tile buffers,
+    // the (head, q-block), and this lane's query index, entropy and whether it exists; the
+    // default does nothing.
+    struct NoEpilogue {
+        __device__ void operator()(lds_char_t *, lds_char_t *, lds_char_t *, lds_char_t *, int, int, int, float,
+                                   bool) const {}
+    };
+
+    template <class Epi = NoEpilogue>
+    static __device__ void run(const AttnArgs &a, const Epi &epi = Epi()) {
         constexpr int BQ = NW * 32 * QW;
         __shared__ __attribute__((aligned(1024))) char k0_raw[C::TILE];
         __shared__ __attribute__((aligned(1024))) char k1_raw[C::TILE];
@@ -460,11 +470,13 @@ struct Bf16Kernel {
         }
 
         // combine the two lane halves of each query and write out
+        float hq = 0.f;
 #pragma unroll
         for (int q2 = 0; q2 < QW; ++q2) {
             const float l = pair_sum(x.st[q2].l);
             const float t = ENT ? pair_sum(x.st[q2].t) : 0.f;
             const int qi = q0 + 32 * q2;
+            if (ENT) hq = l > 0.f ? kLn2 * (__log2f(l) - t / l) : 0.f;
             if (qi < N) {
                 const float inv = l > 0.f ? 1.f / l : 0.f;
                 __bf16 *op = static_cast<__bf16 *>(a.o) + head + (int64_t)qi * D;
@@ -479,17 +491,41 @@ struct Bf16Kernel {
                     }
                 if (h == 0) {
                     const int64_t idx = (int64_t)o * N + qi;
-                    if (ENT && a.ent) a.ent[idx] = l > 0.f ? kLn2 * (__log2f(l) - t / l) : 0.f;
+                    if (ENT && a.ent) a.ent[idx] = hq;
                     if (a.lse) a.lse[idx] = l > 0.f ? kLn2 * (x.st[q2].m + __log2f(l)) : -INFINITY;
                 }
             }
         }
+        epi(K0, K1, V0, V1, o, qb, q0 - qb * BQ, hq, q0 < N && h == 0);
+    }
+};
+
+// Mask epilogue of the fused warm-up kernel: the q-block's mask row is built as soon as its
+// entropies are final, in the attention kernel's own LDS ("Token Radius Attention for
+// Efficient Video Generation", section 2, TRA pipeline steps 2-3 fused with the entropy
+// pass of step 1): no launch, and no entropy read back from HBM.
+template <int RR>
+struct MaskEpilogue {
+    const MaskArgs *m;
+    __device__ void operator()(lds_char_t *k0, lds_char_t *k1, lds_char_t *v0, lds_char_t *v1, int o, int qb, int qlocal,
+                               float hq, bool valid) const {
+        using namespace maskdev;
+        const MaskLds<128, true> L((void *)k0, (void *)k1, (void *)v1, (void *)v0, m->g.F, m->nqf_max);
+        __syncthreads();  // every wavefront is past its last read of the tiles
+        if (valid) L.H[qlocal] = hq;
+        mask_qblock<128, RR, true, true>(*m, L, o, qb);
     }
 };
 
 template <int D, int NW, int QW, bool SPARSE, bool ENT>
 __global__ __launch_bounds__(NW * 64, QW == 1 ? 2 : 1) void attn_bf16_kernel(AttnArgs a) {
     Bf16Kernel<D, NW, QW, SPARSE, ENT>::run(a);
+}
+
+// dense attention + entropy + mask row, one workgroup per 128-query block (D = 128, bf16)
+template <int RR>
+__global__ __launch_bounds__(256, 2) void attn_mask_kernel(AttnArgs a, MaskArgs m) {
+    Bf16Kernel<128, 4, 1, false, true>::run(a, MaskEpilogue<RR>{&m});
 }
 
 // ----------------------------------------------------------------------------------
@@ -640,6 +676,18 @@ hipError_t launch_d(const AttnArgs &a, int dtype, bool sparse, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_dense_mask(const AttnArgs &a, const MaskArgs &m, hipStream_t s) {
+    const unsigned blocks = (unsigned)((int64_t)a.outer * a.nqb);
+    switch (m.t.rmax) {
+        case 1: attn_mask_kernel<1><<<blocks, 256, 0, s>>>(a, m); break;
+        case 2: attn_mask_kernel<2><<<blocks, 256, 0, s>>>(a, m); break;
+        case 3: attn_mask_kernel<3><<<blocks, 256, 0, s>>>(a, m); break;
+        case 4: attn_mask_kernel<4><<<blocks, 256, 0, s>>>(a, m); break;
+        default: attn_mask_kernel<0><<<blocks, 256, 0, s>>>(a, m); break;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_attention(const AttnArgs &a, int D, int dtype, int block_q, bool sparse, hipStream_t s) {
     // bf16: 32 * kQW queries per wavefront; fp32: 32 queries per wavefront

@@ -336,6 +336,46 @@ tra_status tra_build_block_mask(const float *entropy, int outer, int F, int H, i
     return from_hip(tra::launch_build_mask(a, s), "build mask");
 }
 
+tra_status tra_dense_attn_entropy_mask(const void *q, const void *k, const void *v, void *o, float *entropy,
+                                       float *lse, int outer, int F, int H, int W, int D, tra_dtype dt,
+                                       float sm_scale, float tau, float gamma, int block_q, int block_k,
+                                       int vote_threshold, int tile_h, int tile_w, int32_t *kv_count,
+                                       int32_t *kv_index, int64_t kv_index_capacity, uint8_t *block_mask,
+                                       hipStream_t s) {
+    if (!kv_count || !kv_index || outer < 1 || vote_threshold < 1) return TRA_ERR_INVALID_ARG;
+    TileGeom g;
+    tra_status st = check_mask_args(F, H, W, tau, gamma, block_q, block_k, tile_h, tile_w, g);
+    if (st != TRA_OK) return st;
+    st = check_attn_common(q, k, v, o, outer, g.N, D, dt, sm_scale);
+    if (st != TRA_OK) return st;
+    if (dt != TRA_BF16 || D != 128 || block_q != 128 || block_k != 64) return TRA_ERR_UNSUPPORTED;
+    if (!tra::mask_fits_split(block_q, F, g.HW)) return TRA_ERR_UNSUPPORTED;
+    const int nqb = (g.N + block_q - 1) / block_q;
+    const int nkb = (g.N + block_k - 1) / block_k;
+    if ((int64_t)outer * nqb > ((int64_t)1 << 31) - 1) return TRA_ERR_UNSUPPORTED;
+    if (kv_index_capacity < (int64_t)outer * nqb * nkb) return TRA_ERR_CAPACITY;
+    tra::MaskArgs m{};
+    st = get_tables(g, tau, gamma, block_k, m.t);
+    if (st != TRA_OK) return st;
+    m.ent = entropy;
+    m.outer = outer; m.nqb = nqb; m.nkb = nkb;
+    m.block_q = block_q; m.block_k = block_k; m.vote = vote_threshold;
+    m.nqf_max = tra::mask_frames_per_qblock(block_q, g.HW, F);
+    m.chunk = std::min(256, tra::kMaskEntryCap / std::max(1, m.t.rmax));
+    m.g = g;
+    m.kv_count = kv_count; m.kv_index = kv_index; m.block_mask = block_mask;
+    tra::AttnArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    a.ent = entropy; a.lse = lse;
+    a.outer = outer; a.N = g.N;
+    a.nqb = nqb;
+    a.nkb = nkb;
+    a.sm_scale = sm_scale;
+    a.c = (float)((double)sm_scale * 1.4426950408889634074);
+    clear_pending_error();
+    return from_hip(tra::launch_dense_mask(a, m, s), "dense attention with mask");
+}
+
 tra_status tra_block_sparse_attn(const void *q, const void *k, const void *v, void *o, float *lse,
                                  const int32_t *kv_count, const int32_t *kv_index, int outer, int N, int D,
                                  tra_dtype dt, float sm_scale, int block_q, int block_k, hipStream_t s) {

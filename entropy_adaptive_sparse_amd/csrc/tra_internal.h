@@ -75,6 +75,8 @@ struct MaskArgs {
 hipError_t launch_build_mask(const MaskArgs &a, hipStream_t s);
 int mask_frames_per_qblock(int block_q, int HW, int F);
 size_t mask_lds_bytes(int block_q, int F, int HW);
+// whether the mask state fits the four 16 KB tile buffers of the attention kernel (fused path)
+bool mask_fits_split(int block_q, int F, int HW);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {
@@ -89,5 +91,8 @@ struct AttnArgs {
 
 // dtype: 0 = fp32, 1 = bf16.  sparse: walk kv_index; else every k-block (dense).
 hipError_t launch_attention(const AttnArgs &a, int D, int dtype, int block_q, bool sparse, hipStream_t s);
+
+// dense attention + entropy with the mask builder as epilogue (bf16, D = 128, block_q = 128)
+hipError_t launch_dense_mask(const AttnArgs &a, const MaskArgs &m, hipStream_t s);
 
 }  // namespace tra

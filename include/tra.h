@@ -157,6 +157,32 @@ tra_status tra_block_sparse_attn(const void *q, const void *k, const void *v, vo
                                  const int32_t *kv_count, const int32_t *kv_index, int outer, int N, int D,
                                  tra_dtype dt, float sm_scale, int block_q, int block_k, hipStream_t s);
 
+/*
+ * Warm-up pass with the mask fused in: tra_dense_attn_entropy followed by
+ * tra_build_block_mask on its entropies, in one kernel ("Token Radius
+ * Attention for Efficient Video Generation", section 2, TRA pipeline: the
+ * entropy of step 1 feeds the radius mapping and the fused mask kernel of
+ * steps 2-3; section 3, the entropy and mask kernels co-designed to keep the
+ * overhead small).  A workgroup builds its q-block's mask row as soon as that
+ * q-block's entropies are final, in its own on-chip memory.
+ *
+ * Results equal those of the two separate calls bit for bit: o, entropy and
+ * lse as tra_dense_attn_entropy writes them; kv_count, kv_index and
+ * block_mask as tra_build_block_mask writes them from that entropy.
+ * Arguments: as in those two calls, with N = F*H*W; entropy and lse may be
+ * NULL (the mask still uses the entropies).  Supported: bf16, D = 128,
+ * block_q = 128, block_k = 64, and geometries whose per-q-block mask state
+ * fits the kernel's tile buffers (at most 64 frames); anything else returns
+ * TRA_ERR_UNSUPPORTED before any HIP call.  The first call for a geometry
+ * uploads the mask tables synchronously (see tra_mask_prepare).
+ */
+tra_status tra_dense_attn_entropy_mask(const void *q, const void *k, const void *v, void *o, float *entropy,
+                                       float *lse, int outer, int F, int H, int W, int D, tra_dtype dt,
+                                       float sm_scale, float tau, float gamma, int block_q, int block_k,
+                                       int vote_threshold, int tile_h, int tile_w, int32_t *kv_count,
+                                       int32_t *kv_index, int64_t kv_index_capacity, uint8_t *block_mask,
+                                       hipStream_t s);
+
 #ifdef __cplusplus
 }
 #endif

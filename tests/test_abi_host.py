@@ -35,7 +35,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
-              "tra_build_block_mask", "tra_block_sparse_attn", "tra_mask_prepare", "tra_status_string"):
+              "tra_build_block_mask", "tra_block_sparse_attn", "tra_mask_prepare", "tra_status_string",
+              "tra_dense_attn_entropy_mask"):
         assert n in names
 
 
@@ -125,3 +126,28 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 8, 4)
     with pytest.raises(ValueError):
         tra.tile_major_permute(x, 1, 2, 4)
+
+
+def test_fused_warmup_validation(lib):
+    f = lib.tra_dense_attn_entropy_mask
+    # q k v o H lse outer F H W D dt scale tau gamma bq bk vote th tw cnt idx cap mask stream
+    base = [FAKE, FAKE2, FAKE3, FAKE4, None, None, 2, 4, 16, 16, 128, BF16, 0.088, 0.03, 0.5, 128, 64, 1, 8, 8,
+            FAKE + 64, FAKE2 + 64, 2 * 8 * 16, None, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a20=None) == INVALID                         # kv_count
+    assert call(a21=None) == INVALID                         # kv_index
+    assert call(a0=None) == INVALID                          # q
+    assert call(a3=FAKE) == INVALID                          # o aliases q
+    assert call(a17=0) == INVALID                            # vote threshold
+    assert call(a13=0.0) == INVALID                          # tau
+    assert call(a11=F32) == UNSUPPORTED                      # fp32
+    assert call(a10=64) == UNSUPPORTED                       # D = 64
+    assert call(a15=64) == UNSUPPORTED                       # block_q = 64
+    assert call(a16=32) == UNSUPPORTED                       # block_k
+    assert call(a7=65, a8=8, a9=8) == UNSUPPORTED            # more frames than the tile buffers hold
+    assert call(a22=2 * 8 * 16 - 1) == CAPACITY              # kv_index capacity
