@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", type=int, default=3)
     p.add_argument("--tau", type=float, default=None)
+    p.add_argument("--density", type=float, default=None,
+                   help="use the oracle-calibrated tau for this retained density (0.09, 0.15, 0.19 at workload 3)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -149,6 +151,11 @@ def main():
     dev = torch.device("cuda:0")
     wl = workloads.get(args.workload)
     tau = wl.tau if args.tau is None else args.tau
+    if args.density is not None:
+        if args.density not in workloads.DENSITY_TAU.get(wl.wid, {}):
+            sys.exit("no calibrated tau for density %g at workload %d (have %s)"
+                     % (args.density, wl.wid, sorted(workloads.DENSITY_TAU.get(wl.wid, {}))))
+        tau = workloads.DENSITY_TAU[wl.wid][args.density]
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
 
     t0 = time.time()
@@ -217,6 +224,18 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     ms_dense_plain = e0.elapsed_time(e1) / 2
+    # cold variant of the sparse call: 512 MB written between calls (the last-level cache is 256 MB)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(3):
+        scratch.fill_(1)
+        e0.record()
+        tra.block_sparse_attn(qp, kp, vp, cnt, idx, wl.block_q, wl.block_k, wl.sm_scale, out=osp)
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del scratch
+    ms_sparse_cold = float(np.mean(cold))
     # the warm-up pass with the mask builder fused in (same outputs as dense_entropy + build_mask)
     ms_fused = None
     if wl.dtype == "bf16" and wl.D == 128 and wl.block_q == 128 and not wl.static_mask:
@@ -268,6 +287,7 @@ def main():
         },
         "ms_per_call": {k2: round(v2, 4) for k2, v2 in ms.items()},
         "ms_dense_no_entropy": round(ms_dense_plain, 4),
+        "ms_sparse_cold": round(ms_sparse_cold, 4),
         "ms_warmup_separate": round(ms["dense_entropy"] + ms["build_mask"], 4),
         "ms_warmup_fused": None if ms_fused is None else round(ms_fused, 4),
         "ms_reuse_step": round(ms["permute_qkv"] + ms["sparse_attn"] + ms["unpermute"], 4),

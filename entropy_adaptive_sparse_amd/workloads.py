@@ -77,5 +77,9 @@ WORKLOADS = {
 }
 
 
+# the headline workload at the ends of the 9-19% retained range (same calibration)
+DENSITY_TAU = {3: {0.09: 3.57e-3, 0.15: 3.01e-2, 0.19: 6.95e-2}}
+
+
 def get(wid: int) -> Workload:
     return WORKLOADS[wid]

@@ -9,8 +9,10 @@ reports).  For each workload with a density target:
     to fp32 -- what the GPU pipeline feeds its mask builder;
   - log tau is bisected (a fixed 30 steps) until the oracle's block mask of the sampled
     q-blocks has the target density.
-The static-mask workload (one entropy value for every query, a radial-style mask) bisects
-that value until the density equals the density its base workload reaches at its tau.
+The headline workload is also calibrated to 9% and 19% (the ends of the range the pages
+report).  The static-mask workload (one entropy value for every query, a radial-style mask)
+bisects that value until the density equals the density its base workload reaches at its
+tau.
 
 Run from the repository root:  python tests/golden/calibrate_tau.py
 The values are then frozen in entropy_adaptive_sparse_amd/workloads.py.
@@ -100,6 +102,15 @@ def main():
         result["workloads"][wl.name] = {"tau": tau, "tau_exact": math.exp(log_tau), "density": d,
                                         "target": wl.density_target, "seconds": round(time.time() - t0, 1)}
         print(wl.name, result["workloads"][wl.name], flush=True)
+    # the headline workload at the ends of the reported range
+    wl3 = workloads.get(3)
+    extra = {}
+    for target in (0.09, 0.19):
+        lt = bisect(lambda x: density(wl3, cache[3], math.exp(x)), math.log(1e-6), math.log(10.0), target)
+        tau = float("%.3g" % math.exp(lt))
+        extra["%.2f" % target] = {"tau": tau, "density": density(wl3, cache[3], tau)}
+    result["workloads"][wl3.name]["density_variants"] = extra
+    print(wl3.name, extra, flush=True)
     # static-mask workload: one entropy value for every query of its base workload's samples
     wl5 = workloads.get(5)
     base = workloads.get(3)

@@ -24,3 +24,15 @@ def test_static_mask_workload_matches_calibration():
     assert wl.static_mask and wl.static_entropy == c["static_entropy"] and wl.tau == c["tau"]
     assert abs(c["density"] - c["target"]) < 0.005
     assert wl.tau == workloads.get(3).tau
+
+
+def test_density_variants_match_calibration():
+    cal = json.load(open(GOLDEN))["workloads"]
+    wl = workloads.get(3)
+    var = cal[wl.name]["density_variants"]
+    for d, tau in workloads.DENSITY_TAU[3].items():
+        if abs(d - 0.15) < 1e-9:
+            assert tau == wl.tau
+            continue
+        c = var["%.2f" % d]
+        assert tau == c["tau"] and abs(c["density"] - d) < 0.005
