@@ -173,9 +173,13 @@ struct Bf16Cfg {
 // slots are the DMA consecutive 64-slot ranges starting at slot 64 * DMA * wave.
 template <int NDMA>
 __device__ inline void dma_tile(const char *__restrict__ src, lds_char_t *dst, const int *soff, int wave) {
+    // a uniform base plus a zero-extended 32-bit lane offset selects the copy's SGPR-base form
+    // (no 64-bit address arithmetic per copy), and a uniform wavefront index keeps the LDS
+    // destination (M0) in scalar registers
+    const int w = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
     for (int i = 0; i < NDMA; ++i)
-        __builtin_amdgcn_global_load_lds(src + soff[i], dst + (wave * NDMA + i) * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src + (uint64_t)(uint32_t)soff[i], dst + (w * NDMA + i) * 1024, 16, 0, 0);
 }
 
 // copy the tile of 64 keys starting at key0; rows past N in a ragged last tile are
