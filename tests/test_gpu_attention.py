@@ -258,3 +258,37 @@ def test_sparse_full_size_sampled(orc, wid):
     heads = synth.uniform_ints(wid + 30, 2, 0, wl.outer)
     mask = _oracle_masks(orc, ent, wl, heads, qblocks=blocks)
     _check_sparse(orc, wl, q, k, v, o, L, mask, heads, rows)
+
+
+@pytest.mark.parametrize("dtype,slope", [("bf16", 2.0), ("f32", 2.0), ("bf16", -2.0)])
+def test_rising_scores_force_max_moves(orc, dtype, slope):
+    # scores grow (or fall) along the natural key order by ~0.2 nats per key (~13 nats per
+    # 64 keys), so a rising max outgrows the running reference by more than the lazy
+    # threshold (2^8) in almost every tile: the O / l / t rescale runs tile after tile (dense
+    # with entropy, and sparse over every block), and the result must still match the
+    # two-pass oracle
+    torch = torch_mod()
+    t = tra()
+    F, H, W, D = 1, 16, 40, 128
+    N = F * H * W
+    wl = small_workload(300, F, H, W, D, dtype, outer=1)
+    g = np.random.default_rng(7)
+    q = np.zeros((1, N, D), dtype=np.float32)
+    q[0, :, 0] = 4.0 + g.uniform(0.0, 1.0, N)
+    q[0, :, 1:] = 0.1 * g.standard_normal((N, D - 1))
+    k = 0.1 * g.standard_normal((1, N, D)).astype(np.float32)
+    k[0, :, 0] = slope * np.arange(N) / 4.0
+    v = g.standard_normal((1, N, D)).astype(np.float32)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    qt, kt, vt = (torch.from_numpy(x).to(dt) for x in (q, k, v))
+    o, Hh, L = _run_dense(t, wl, qt, kt, vt)
+    _check_dense(orc, wl, qt, kt, vt, o, Hh, L, heads=[0])
+    dev = device()
+    qp, kp, vp = _to_gpu_tile_major(t, wl, qt, kt, vt)
+    nqb, nkb = -(-N // wl.block_q), -(-N // wl.block_k)
+    cnt = torch.full((1, nqb), nkb, dtype=torch.int32, device=dev)
+    idx = torch.arange(nkb, dtype=torch.int32, device=dev).repeat(1, nqb, 1).contiguous()
+    os_, Ls = t.block_sparse_attn(qp, kp, vp, cnt, idx, wl.block_q, wl.block_k, wl.sm_scale, lse=True)
+    od, _, Ld = t.dense_attn_entropy(qp, kp, vp, wl.sm_scale, entropy=False, lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(os_, od) and torch.equal(Ls, Ld)  # every block retained: the dense result, bit for bit
