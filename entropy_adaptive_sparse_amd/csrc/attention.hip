@@ -24,7 +24,10 @@
 // Per-query statistics stay inside one lane; the two lanes that share a query combine
 // with one v_permlane32_swap.  K and V tiles are copied global -> LDS directly (no
 // staging registers) into double buffers while the current tile is computed; one
-// barrier per tile.
+// barrier per tile.  Workgroups are ordered so that the 8 XCDs work through the same
+// heads together, each on runs of neighbouring q-blocks.  The warm-up variant
+// attn_mask_kernel ends with the mask builder (mask_impl.h) for its own q-block, run in
+// the freed tile buffers (TRA pipeline steps 2-3 fused into the entropy pass).
 #include "mask_impl.h"
 #include "tra_internal.h"
 
