@@ -260,6 +260,41 @@ tra_status permute_impl(const void *src, void *dst, int outer, int F, int H, int
                     "permute");
 }
 
+// Mask arguments after check_mask_args succeeded: sizes, capacity, tables (first use uploads).
+tra_status fill_mask_args(const TileGeom &g, const float *entropy, int outer, float tau, float gamma, int block_q,
+                          int block_k, int vote_threshold, int32_t *kv_count, int32_t *kv_index,
+                          int64_t kv_index_capacity, uint8_t *block_mask, tra::MaskArgs &m) {
+    const int nqb = (g.N + block_q - 1) / block_q;
+    const int nkb = (g.N + block_k - 1) / block_k;
+    if ((int64_t)outer * nqb > ((int64_t)1 << 31) - 1) return TRA_ERR_UNSUPPORTED;
+    if (kv_index_capacity < (int64_t)outer * nqb * nkb) return TRA_ERR_CAPACITY;
+    m = tra::MaskArgs{};
+    const tra_status st = get_tables(g, tau, gamma, block_k, m.t);
+    if (st != TRA_OK) return st;
+    m.ent = entropy;
+    m.outer = outer; m.nqb = nqb; m.nkb = nkb;
+    m.block_q = block_q; m.block_k = block_k; m.vote = vote_threshold;
+    m.nqf_max = tra::mask_frames_per_qblock(block_q, g.HW, g.F);
+    m.chunk = std::min(256, tra::kMaskEntryCap / std::max(1, m.t.rmax));
+    m.g = g;
+    m.kv_count = kv_count; m.kv_index = kv_index; m.block_mask = block_mask;
+    return TRA_OK;
+}
+
+// Attention arguments (nqb / nkb for 128-query and 64-key blocks; a launcher may regroup).
+tra::AttnArgs attn_args(const void *q, const void *k, const void *v, void *o, float *entropy, float *lse, int outer,
+                        int N, float sm_scale) {
+    tra::AttnArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    a.ent = entropy; a.lse = lse;
+    a.outer = outer; a.N = N;
+    a.nqb = (N + 127) / 128;
+    a.nkb = (N + 63) / 64;
+    a.sm_scale = sm_scale;
+    a.c = (float)((double)sm_scale * 1.4426950408889634074);
+    return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -289,14 +324,7 @@ tra_status tra_dense_attn_entropy(const void *q, const void *k, const void *v, v
                                   int outer, int N, int D, tra_dtype dt, float sm_scale, hipStream_t s) {
     const tra_status st = check_attn_common(q, k, v, o, outer, N, D, dt, sm_scale);
     if (st != TRA_OK) return st;
-    tra::AttnArgs a{};
-    a.q = q; a.k = k; a.v = v; a.o = o;
-    a.ent = entropy; a.lse = lse;
-    a.outer = outer; a.N = N;
-    a.nqb = (N + 127) / 128;
-    a.nkb = (N + 63) / 64;
-    a.sm_scale = sm_scale;
-    a.c = (float)((double)sm_scale * 1.4426950408889634074);
+    const tra::AttnArgs a = attn_args(q, k, v, o, entropy, lse, outer, N, sm_scale);
     clear_pending_error();
     return from_hip(tra::launch_attention(a, D, dt == TRA_BF16 ? 1 : 0, 128, false, s), "dense attention");
 }
@@ -316,24 +344,14 @@ tra_status tra_build_block_mask(const float *entropy, int outer, int F, int H, i
                                 uint8_t *block_mask, hipStream_t s) {
     if (!entropy || !kv_count || !kv_index || outer < 1 || vote_threshold < 1) return TRA_ERR_INVALID_ARG;
     TileGeom g;
-    const tra_status st = check_mask_args(F, H, W, tau, gamma, block_q, block_k, tile_h, tile_w, g);
+    tra_status st = check_mask_args(F, H, W, tau, gamma, block_q, block_k, tile_h, tile_w, g);
     if (st != TRA_OK) return st;
-    const int nqb = (g.N + block_q - 1) / block_q;
-    const int nkb = (g.N + block_k - 1) / block_k;
-    if ((int64_t)outer * nqb > ((int64_t)1 << 31) - 1) return TRA_ERR_UNSUPPORTED;
-    if (kv_index_capacity < (int64_t)outer * nqb * nkb) return TRA_ERR_CAPACITY;
-    tra::MaskArgs a{};
-    const tra_status ts = get_tables(g, tau, gamma, block_k, a.t);
-    if (ts != TRA_OK) return ts;
-    a.ent = entropy;
-    a.outer = outer; a.nqb = nqb; a.nkb = nkb;
-    a.block_q = block_q; a.block_k = block_k; a.vote = vote_threshold;
-    a.nqf_max = tra::mask_frames_per_qblock(block_q, g.HW, F);
-    a.chunk = std::min(256, tra::kMaskEntryCap / std::max(1, a.t.rmax));
-    a.g = g;
-    a.kv_count = kv_count; a.kv_index = kv_index; a.block_mask = block_mask;
+    tra::MaskArgs m;
+    st = fill_mask_args(g, entropy, outer, tau, gamma, block_q, block_k, vote_threshold, kv_count, kv_index,
+                        kv_index_capacity, block_mask, m);
+    if (st != TRA_OK) return st;
     clear_pending_error();
-    return from_hip(tra::launch_build_mask(a, s), "build mask");
+    return from_hip(tra::launch_build_mask(m, s), "build mask");
 }
 
 tra_status tra_dense_attn_entropy_mask(const void *q, const void *k, const void *v, void *o, float *entropy,
@@ -350,28 +368,11 @@ tra_status tra_dense_attn_entropy_mask(const void *q, const void *k, const void 
     if (st != TRA_OK) return st;
     if (dt != TRA_BF16 || D != 128 || block_q != 128 || block_k != 64) return TRA_ERR_UNSUPPORTED;
     if (!tra::mask_fits_split(block_q, F, g.HW)) return TRA_ERR_UNSUPPORTED;
-    const int nqb = (g.N + block_q - 1) / block_q;
-    const int nkb = (g.N + block_k - 1) / block_k;
-    if ((int64_t)outer * nqb > ((int64_t)1 << 31) - 1) return TRA_ERR_UNSUPPORTED;
-    if (kv_index_capacity < (int64_t)outer * nqb * nkb) return TRA_ERR_CAPACITY;
-    tra::MaskArgs m{};
-    st = get_tables(g, tau, gamma, block_k, m.t);
+    tra::MaskArgs m;
+    st = fill_mask_args(g, entropy, outer, tau, gamma, block_q, block_k, vote_threshold, kv_count, kv_index,
+                        kv_index_capacity, block_mask, m);
     if (st != TRA_OK) return st;
-    m.ent = entropy;
-    m.outer = outer; m.nqb = nqb; m.nkb = nkb;
-    m.block_q = block_q; m.block_k = block_k; m.vote = vote_threshold;
-    m.nqf_max = tra::mask_frames_per_qblock(block_q, g.HW, F);
-    m.chunk = std::min(256, tra::kMaskEntryCap / std::max(1, m.t.rmax));
-    m.g = g;
-    m.kv_count = kv_count; m.kv_index = kv_index; m.block_mask = block_mask;
-    tra::AttnArgs a{};
-    a.q = q; a.k = k; a.v = v; a.o = o;
-    a.ent = entropy; a.lse = lse;
-    a.outer = outer; a.N = g.N;
-    a.nqb = nqb;
-    a.nkb = nkb;
-    a.sm_scale = sm_scale;
-    a.c = (float)((double)sm_scale * 1.4426950408889634074);
+    const tra::AttnArgs a = attn_args(q, k, v, o, entropy, lse, outer, g.N, sm_scale);
     clear_pending_error();
     return from_hip(tra::launch_dense_mask(a, m, s), "dense attention with mask");
 }
@@ -384,15 +385,9 @@ tra_status tra_block_sparse_attn(const void *q, const void *k, const void *v, vo
     if (!kv_count || !kv_index) return TRA_ERR_INVALID_ARG;
     if (block_q < 1 || block_k < 1) return TRA_ERR_INVALID_ARG;
     if ((block_q != 64 && block_q != 128) || block_k != 64) return TRA_ERR_UNSUPPORTED;
-    tra::AttnArgs a{};
-    a.q = q; a.k = k; a.v = v; a.o = o;
-    a.ent = nullptr; a.lse = lse;
+    tra::AttnArgs a = attn_args(q, k, v, o, nullptr, lse, outer, N, sm_scale);
     a.kv_count = kv_count; a.kv_index = kv_index;
-    a.outer = outer; a.N = N;
     a.nqb = (N + block_q - 1) / block_q;
-    a.nkb = (N + block_k - 1) / block_k;
-    a.sm_scale = sm_scale;
-    a.c = (float)((double)sm_scale * 1.4426950408889634074);
     clear_pending_error();
     return from_hip(tra::launch_attention(a, D, dt == TRA_BF16 ? 1 : 0, block_q, true, s), "sparse attention");
 }
