@@ -13,6 +13,8 @@ Functions (names as in the C ABI, without the ``tra_`` prefix):
     dense_attn_entropy_mask (the warm-up pass with the mask builder fused in)
     build_block_mask, mask_prepare
     block_sparse_attn
+    dense_attn_entropy_natural, block_sparse_attn_natural (natural-order q, k, v, o; the
+        tile-major map applied inside the kernels' loads and stores)
 """
 from __future__ import annotations
 
@@ -22,7 +24,8 @@ import threading
 
 __all__ = [
     "TraError", "library_path", "load", "tile_major_permute", "tile_major_unpermute", "dense_attn_entropy",
-    "dense_attn_entropy_mask", "build_block_mask", "mask_prepare", "block_sparse_attn", "exported_symbols",
+    "dense_attn_entropy_mask", "build_block_mask", "mask_prepare", "block_sparse_attn",
+    "dense_attn_entropy_natural", "block_sparse_attn_natural", "exported_symbols",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -74,9 +77,14 @@ def load():
         lib.tra_block_sparse_attn.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, f32, i32, i32, P]
         lib.tra_dense_attn_entropy_mask.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f32, f32, f32,
                                                     i32, i32, i32, i32, i32, P, P, i64, P, P]
+        lib.tra_dense_attn_entropy_natural.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f32, i32,
+                                                       i32, P]
+        lib.tra_block_sparse_attn_natural.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f32, i32,
+                                                      i32, i32, i32, P]
         for name in ("tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
                      "tra_build_block_mask", "tra_mask_prepare", "tra_block_sparse_attn",
-                     "tra_dense_attn_entropy_mask"):
+                     "tra_dense_attn_entropy_mask", "tra_dense_attn_entropy_natural",
+                     "tra_block_sparse_attn_natural"):
             getattr(lib, name).restype = i32
         _lib = lib
         return lib
@@ -84,7 +92,8 @@ def load():
 
 def exported_symbols():
     return ["tra_status_string", "tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
-            "tra_build_block_mask", "tra_mask_prepare", "tra_block_sparse_attn", "tra_dense_attn_entropy_mask"]
+            "tra_build_block_mask", "tra_mask_prepare", "tra_block_sparse_attn", "tra_dense_attn_entropy_mask",
+            "tra_dense_attn_entropy_natural", "tra_block_sparse_attn_natural"]
 
 
 # ------------------------------------------------------------------------------------------------
@@ -256,4 +265,52 @@ def block_sparse_attn(q, k, v, kv_count, kv_index, block_q: int = 128, block_k: 
     scale = (1.0 / D ** 0.5) if sm_scale is None else float(sm_scale)
     _call("tra_block_sparse_attn", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), _ptr(kv_count), _ptr(kv_index),
           outer, N, D, _dt(q), scale, block_q, block_k, _stream(q))
+    return o, L
+
+
+def dense_attn_entropy_natural(q, k, v, F: int, H: int, W: int, sm_scale: float | None = None, entropy: bool = True,
+                               lse: bool = False, tile_h: int = 8, tile_w: int = 8, out=None, ent_out=None,
+                               lse_out=None):
+    """dense_attn_entropy on natural-order q, k, v; o in natural order, H and lse indexed by tile-major
+    position.  Returns (o, H, lse)."""
+    torch = _torch()
+    outer, N, D = _check_qkv(q, k, v)
+    if N != F * H * W:
+        raise ValueError("N must equal F*H*W")
+    o = torch.empty_like(q) if out is None else _dev(out, "out")
+    Hh = None
+    if entropy:
+        Hh = torch.empty((outer, N), dtype=torch.float32, device=q.device) if ent_out is None else ent_out
+    L = None
+    if lse:
+        L = torch.empty((outer, N), dtype=torch.float32, device=q.device) if lse_out is None else lse_out
+    scale = (1.0 / D ** 0.5) if sm_scale is None else float(sm_scale)
+    _call("tra_dense_attn_entropy_natural", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(Hh), _ptr(L), outer, F, H, W,
+          D, _dt(q), scale, tile_h, tile_w, _stream(q))
+    return o, Hh, L
+
+
+def block_sparse_attn_natural(q, k, v, kv_count, kv_index, F: int, H: int, W: int, block_q: int = 128,
+                              block_k: int = 64, sm_scale: float | None = None, lse: bool = False, tile_h: int = 8,
+                              tile_w: int = 8, out=None, lse_out=None):
+    """block_sparse_attn on natural-order q, k, v (kv_count / kv_index: the tile-major block lists);
+    o in natural order, lse indexed by tile-major position.  Returns (o, lse)."""
+    torch = _torch()
+    outer, N, D = _check_qkv(q, k, v)
+    if N != F * H * W:
+        raise ValueError("N must equal F*H*W")
+    _dev(kv_count, "kv_count")
+    _dev(kv_index, "kv_index")
+    nqb, nkb = -(-N // block_q), -(-N // block_k)
+    if tuple(kv_count.shape) != (outer, nqb) or tuple(kv_index.shape) != (outer, nqb, nkb):
+        raise ValueError("kv_count/kv_index shape does not match N, block_q, block_k")
+    if kv_count.dtype != torch.int32 or kv_index.dtype != torch.int32:
+        raise ValueError("kv_count/kv_index must be int32")
+    o = torch.empty_like(q) if out is None else _dev(out, "out")
+    L = None
+    if lse:
+        L = torch.empty((outer, N), dtype=torch.float32, device=q.device) if lse_out is None else lse_out
+    scale = (1.0 / D ** 0.5) if sm_scale is None else float(sm_scale)
+    _call("tra_block_sparse_attn_natural", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), _ptr(kv_count),
+          _ptr(kv_index), outer, F, H, W, D, _dt(q), scale, block_q, block_k, tile_h, tile_w, _stream(q))
     return o, L

@@ -172,6 +172,23 @@ struct Bf16Cfg {
     static __device__ inline int fV(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
+// A copy's 32-bit lane offset, zero-extended.  The empty asm hides where the value comes
+// from, so the compiler cannot fold the uniform table offset into a loop-invariant 64-bit
+// vector address; the copy keeps the SGPR-base form: uniform base + this offset.
+__device__ inline uint64_t lane_offset(int off) {
+    asm volatile("" : "+v"(off));
+    return (uint64_t)(uint32_t)off;
+}
+
+// lane i's value of v, uniform (the host pass of the compiler does not know the builtin)
+__device__ inline int lane_value(int v, int i) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_readlane(v, i);
+#else
+    return v + 0 * i;
+#endif
+}
+
 // direct global -> LDS copy of one tile; src: the tile's first byte; the wavefront's
 // slots are the DMA consecutive 64-slot ranges starting at slot 64 * DMA * wave.
 template <int NDMA>
@@ -185,23 +202,57 @@ __device__ inline void dma_tile(const char *__restrict__ src, lds_char_t *dst, c
         __builtin_amdgcn_global_load_lds(src + (uint64_t)(uint32_t)soff[i], dst + (w * NDMA + i) * 1024, 16, 0, 0);
 }
 
-// copy the tile of 64 keys starting at key0; rows past N in a ragged last tile are
-// fetched from row N - 1 (finite values; their scores are masked later)
-template <int D, int NT, bool ISV>
-__device__ inline void fetch_tile(const char *__restrict__ base, int key0, int N, lds_char_t *dst, const int *soff,
-                                  int wave, int lane) {
+// Tile-major row p of a natural-order tensor is natural row nat4[p / 4] + p % 4: every
+// aligned group of four tile-major rows is a run of four natural rows (the row of a tile
+// whose width is a multiple of four).  Read through the constant address space, so a
+// uniform index gives a scalar load.
+typedef const int32_t __attribute__((address_space(4))) *nat_table_t;
+
+__device__ inline int natural_row(nat_table_t nat4, int p) { return nat4[p >> 2] + (p & 3); }
+
+// NAT: lane i < DMA of the result holds the byte offset (natural row * ROW) of row group
+// w * DMA + i of the tile at key0, the groups this wavefront copies; read a step before the
+// copy so that the copy never waits for the table (a vector load, retired with the copies of
+// the step).
+template <int D, int NT>
+__device__ inline int nat_groups(const int32_t *__restrict__ nat4, int key0, int N, int wave, int lane) {
     using C = Bf16Cfg<D, NT>;
+    return nat4[min((key0 >> 2) + wave * C::DMA + min(lane, C::DMA - 1), (N >> 2) - 1)] * C::ROW;
+}
+
+// copy the tile of 64 keys starting at (tile-major) key0; rows past N in a ragged last tile
+// are fetched from row N - 1 (finite values; their scores are masked later).
+// NAT (D = 128): base holds the rows in natural order.  A copy instruction moves four
+// consecutive tile-major rows, one natural run; natv (nat_groups) holds the run's offset in
+// lane i, and soff[i] is relative to the run.  The ragged tile takes per-lane rows.
+template <int D, int NT, bool ISV, bool NAT>
+__device__ inline void fetch_tile(const char *__restrict__ base, nat_table_t nat4, int natv, int key0, int N,
+                                  lds_char_t *dst, const int *soff, int wave, int lane) {
+    using C = Bf16Cfg<D, NT>;
+    static_assert(!NAT || C::NCH == 16, "one copy instruction covers four rows only for D = 128");
     if (key0 + KT <= N) {
-        dma_tile<C::DMA>(base + (int64_t)key0 * C::ROW, dst, soff, wave);
+        if constexpr (NAT) {
+            const int w = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+            for (int i = 0; i < C::DMA; ++i) {
+                const int m = w * C::DMA + i;  // this copy's slots of the LDS tile
+                __builtin_amdgcn_global_load_lds(base + lane_offset(lane_value(natv, i) + soff[i]), dst + m * 1024, 16,
+                                                 0, 0);
+            }
+        } else {
+            dma_tile<C::DMA>(base + (int64_t)key0 * C::ROW, dst, soff, wave);
+        }
     } else {
         int so[C::DMA];
 #pragma unroll
         for (int i = 0; i < C::DMA; ++i) {
             const int sl = (wave * C::DMA + i) * 64 + lane;
             const int row = sl / C::NCH, p = sl % C::NCH;
-            so[i] = min(row, N - 1 - key0) * C::ROW + ((p ^ (ISV ? C::fV(row) : C::fK(row))) << 4);
+            const int swz = (p ^ (ISV ? C::fV(row) : C::fK(row))) << 4;
+            const int r = min(row, N - 1 - key0);
+            so[i] = (NAT ? natural_row(nat4, key0 + r) : r) * C::ROW + swz;
         }
-        dma_tile<C::DMA>(base + (int64_t)key0 * C::ROW, dst, so, wave);
+        dma_tile<C::DMA>(NAT ? base : base + (int64_t)key0 * C::ROW, dst, so, wave);
     }
 }
 
@@ -271,7 +322,11 @@ __device__ inline float tile_max(const f32x16_t (&s)[2][QW], int q2, float c) {
 //      S^T_{j+1} = K_{j+1} Q^T (MFMA), so the exponentials run under both products
 //   c. the max of tile j+1 (taken before its masking: keys past N are clamped duplicates
 //      of a real key and cannot raise it)
-template <int D, int NW, int QW, bool SPARSE, bool ENT>
+//
+// NAT: q, k, v and o are in natural token order and are read and written through the
+// tile-major map (nat4); the entropy and lse stay indexed by tile-major position, and the
+// arithmetic is that of the tile-major kernel on the permuted tensors, bit for bit.
+template <int D, int NW, int QW, bool SPARSE, bool ENT, bool NAT = false>
 struct Bf16Kernel {
     static constexpr int NT = NW * 64;
     using C = Bf16Cfg<D, NT>;
@@ -279,6 +334,9 @@ struct Bf16Kernel {
     struct Ctx {
         const char *kp, *vp;
         const int32_t __attribute__((address_space(4))) *list;
+        nat_table_t nat4;
+        const int32_t *nat4v;   // the same table, for vector loads
+        int natK, natV;         // nat_groups of the tiles the next K and V copies fetch
         int N, nkb, ntiles, wave, lane, h;
         float c;
         int koff[D / 16];
@@ -301,8 +359,12 @@ struct Bf16Kernel {
     // wait for the copies in flight.
     static __device__ inline void step(Ctx &x, int j, lds_char_t *kn, lds_char_t *kd, lds_char_t *vc,
                                        lds_char_t *vd, f32x16_t (&s)[2][QW], f32x16_t (&sn)[2][QW]) {
-        if (j + 2 < x.ntiles) fetch_tile<D, NT, false>(x.kp, key0_of(x, j + 2), x.N, kd, x.soffK, x.wave, x.lane);
-        if (j + 1 < x.ntiles) fetch_tile<D, NT, true>(x.vp, key0_of(x, j + 1), x.N, vd, x.soffV, x.wave, x.lane);
+        int natn = 0;  // NAT: groups of tile j + 3, the K copy of the next step
+        if constexpr (NAT) natn = nat_groups<D, NT>(x.nat4v, key0_of(x, min(j + 3, x.ntiles - 1)), x.N, x.wave, x.lane);
+        if (j + 2 < x.ntiles)
+            fetch_tile<D, NT, false, NAT>(x.kp, x.nat4, x.natK, key0_of(x, j + 2), x.N, kd, x.soffK, x.wave, x.lane);
+        if (j + 1 < x.ntiles)
+            fetch_tile<D, NT, true, NAT>(x.vp, x.nat4, x.natV, key0_of(x, j + 1), x.N, vd, x.soffV, x.wave, x.lane);
 
         // a.
         mask_tail<QW>(s, key0_of(x, j), x.N, x.h);
@@ -367,6 +429,10 @@ struct Bf16Kernel {
             // c.
             x.mt[q2] = tile_max<QW>(sn, q2, c);
         }
+        if constexpr (NAT) {
+            x.natV = x.natK;
+            x.natK = natn;
+        }
         // this step's copies have landed and every wavefront is done reading
         wait_dma();
         __syncthreads();
@@ -409,6 +475,23 @@ struct Bf16Kernel {
         x.vp = reinterpret_cast<const char *>(static_cast<const __bf16 *>(a.v) + head);
         const int q0 = qb * BQ + x.wave * 32 * QW + ql;  // query of block 0 (block q2: + 32 q2)
 
+        x.natK = x.natV = 0;
+        if constexpr (NAT) {
+            x.nat4 = (nat_table_t)a.nat4;
+            x.nat4v = a.nat4;
+        } else {
+            x.nat4 = nullptr;
+            x.nat4v = nullptr;
+        }
+        // row of query q0 + 32 q2 in q and o (its tile-major position unless NAT)
+        int qrow[QW];
+#pragma unroll
+        for (int q2 = 0; q2 < QW; ++q2) {
+            const int qi = q0 + 32 * q2;
+            qrow[q2] = qi;
+            if constexpr (NAT) qrow[q2] = qi < N ? natural_row(x.nat4, qi) : qi;
+        }
+
         // Q^T operands: lane holds queries q0 + 32 q2, dims 16 ks + 8 h .. + 8
 #pragma unroll
         for (int q2 = 0; q2 < QW; ++q2) {
@@ -416,7 +499,7 @@ struct Bf16Kernel {
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) {
                 u32x4_t val = {0u, 0u, 0u, 0u};
-                if (qi < N) val = *reinterpret_cast<const u32x4_t *>(qp + (int64_t)qi * D + ks * 16 + h * 8);
+                if (qi < N) val = *reinterpret_cast<const u32x4_t *>(qp + (int64_t)qrow[q2] * D + ks * 16 + h * 8);
                 x.qf[q2][ks] = __builtin_bit_cast(bf16x8_t, val);
             }
         }
@@ -439,8 +522,9 @@ struct Bf16Kernel {
         for (int i = 0; i < C::DMA; ++i) {
             const int sl = (x.wave * C::DMA + i) * 64 + lane;
             const int row = sl / C::NCH, p = sl % C::NCH;
-            x.soffK[i] = row * C::ROW + ((p ^ C::fK(row)) << 4);
-            x.soffV[i] = row * C::ROW + ((p ^ C::fV(row)) << 4);
+            const int rel = NAT ? row & 3 : row;  // NAT: relative to the copy's run of four rows
+            x.soffK[i] = rel * C::ROW + ((p ^ C::fK(row)) << 4);
+            x.soffV[i] = rel * C::ROW + ((p ^ C::fV(row)) << 4);
         }
 
         if (SPARSE) {
@@ -461,9 +545,16 @@ struct Bf16Kernel {
         f32x16_t s0[2][QW], s1[2][QW];
         if (x.ntiles > 0) {
             const int k0 = key0_of(x, 0);
-            fetch_tile<D, NT, false>(x.kp, k0, N, K0, x.soffK, x.wave, lane);
-            fetch_tile<D, NT, true>(x.vp, k0, N, V0, x.soffV, x.wave, lane);
-            if (x.ntiles > 1) fetch_tile<D, NT, false>(x.kp, key0_of(x, 1), N, K1, x.soffK, x.wave, lane);
+            int n0 = 0;
+            if constexpr (NAT) {
+                n0 = nat_groups<D, NT>(x.nat4v, k0, N, x.wave, lane);
+                x.natV = nat_groups<D, NT>(x.nat4v, key0_of(x, min(1, x.ntiles - 1)), N, x.wave, lane);
+                x.natK = nat_groups<D, NT>(x.nat4v, key0_of(x, min(2, x.ntiles - 1)), N, x.wave, lane);
+            }
+            fetch_tile<D, NT, false, NAT>(x.kp, x.nat4, n0, k0, N, K0, x.soffK, x.wave, lane);
+            fetch_tile<D, NT, true, NAT>(x.vp, x.nat4, n0, k0, N, V0, x.soffV, x.wave, lane);
+            if (x.ntiles > 1)
+                fetch_tile<D, NT, false, NAT>(x.kp, x.nat4, x.natV, key0_of(x, 1), N, K1, x.soffK, x.wave, lane);
             wait_dma();
             __syncthreads();
             qk_tile<D, NT, QW>(s0, K0, x.koff, x.qf);
@@ -486,7 +577,7 @@ struct Bf16Kernel {
             if (ENT) hq = l > 0.f ? kLn2 * (__log2f(l) - t / l) : 0.f;
             if (qi < N) {
                 const float inv = l > 0.f ? 1.f / l : 0.f;
-                __bf16 *op = static_cast<__bf16 *>(a.o) + head + (int64_t)qi * D;
+                __bf16 *op = static_cast<__bf16 *>(a.o) + head + (int64_t)qrow[q2] * D;
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -524,9 +615,9 @@ struct MaskEpilogue {
     }
 };
 
-template <int D, int NW, int QW, bool SPARSE, bool ENT>
+template <int D, int NW, int QW, bool SPARSE, bool ENT, bool NAT = false>
 __global__ __launch_bounds__(NW * 64, (QW == 1 && NW <= 4) ? 2 : 1) void attn_bf16_kernel(AttnArgs a) {
-    Bf16Kernel<D, NW, QW, SPARSE, ENT>::run(a);
+    Bf16Kernel<D, NW, QW, SPARSE, ENT, NAT>::run(a);
 }
 
 // dense attention + entropy + mask row, one workgroup per 128-query block (D = 128, bf16)
@@ -692,6 +783,23 @@ hipError_t launch_dense_mask(const AttnArgs &a, const MaskArgs &m, hipStream_t s
         case 3: attn_mask_kernel<3><<<blocks, 256, 0, s>>>(a, m); break;
         case 4: attn_mask_kernel<4><<<blocks, 256, 0, s>>>(a, m); break;
         default: attn_mask_kernel<0><<<blocks, 256, 0, s>>>(a, m); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_attention_natural(const AttnArgs &a, bool sparse, hipStream_t s) {
+    if (sparse) {
+        const unsigned blocks = (unsigned)((int64_t)a.outer * a.nqb);
+        attn_bf16_kernel<128, 4, 1, true, false, true><<<blocks, 256, 0, s>>>(a);
+    } else {
+        // as the tile-major dense kernels: 8 wavefronts, 256 queries per workgroup
+        AttnArgs b = a;
+        b.nqb = (a.N + 255) / 256;
+        const unsigned blocks = (unsigned)((int64_t)b.outer * b.nqb);
+        if (a.ent)
+            attn_bf16_kernel<128, 8, 1, false, true, true><<<blocks, 512, 0, s>>>(b);
+        else
+            attn_bf16_kernel<128, 8, 1, false, false, true><<<blocks, 512, 0, s>>>(b);
     }
     return hipGetLastError();
 }

@@ -8,6 +8,7 @@
 #include "../../include/tra.h"
 #include "tra_internal.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -215,6 +216,67 @@ tra_status get_tables(const TileGeom &g, float tau, float gamma, int bk, tra::Ma
     return TRA_OK;
 }
 
+// ------------------------------------------------------------------ natural-order map
+// nat4[g] = natural row of tile-major position 4 g, for kernels that read and write
+// natural-order tensors through the tile-major map.  Valid only when every aligned group
+// of four tile-major positions is a run of four consecutive natural rows, which holds when
+// W and the tile width are multiples of four; anything else is reported as unsupported
+// (and checked here position by position).
+struct NatKey {
+    int dev, F, H, W, th, tw;
+    bool operator<(const NatKey &o) const {
+        return std::tie(dev, F, H, W, th, tw) < std::tie(o.dev, o.F, o.H, o.W, o.th, o.tw);
+    }
+};
+std::map<NatKey, void *> g_nat;
+
+tra_status get_nat_table(const TileGeom &g, const int32_t *&out) {
+    if (g.W % 4 != 0 || g.tw % 4 != 0) return TRA_ERR_UNSUPPORTED;
+    int dev = 0;
+    const hipError_t de = hipGetDevice(&dev);
+    if (de != hipSuccess) return from_hip(de, "hipGetDevice");
+    const NatKey key{dev, g.F, g.H, g.W, g.th, g.tw};
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_nat.find(key);
+    if (it != g_nat.end()) {
+        out = static_cast<const int32_t *>(it->second);
+        return TRA_OK;
+    }
+    std::vector<int32_t> nat4;
+    try {
+        nat4.resize((size_t)g.N / 4);
+    } catch (const std::bad_alloc &) {
+        return TRA_ERR_CAPACITY;
+    }
+    for (int q = 0; q < g.N / 4; ++q) {
+        const int n0 = tra::tile_major_to_natural(4 * q, g);
+        for (int j = 1; j < 4; ++j)
+            if (tra::tile_major_to_natural(4 * q + j, g) != n0 + j) return TRA_ERR_UNSUPPORTED;
+        nat4[(size_t)q] = n0;
+    }
+    void *mem = nullptr;
+    const hipError_t me = hipMalloc(&mem, std::max<size_t>(1, nat4.size()) * sizeof(int32_t));
+    if (me != hipSuccess) return from_hip(me, "hipMalloc of the natural-order map");
+    const hipError_t ce = hipMemcpy(mem, nat4.data(), nat4.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+    if (ce != hipSuccess) {
+        (void)hipFree(mem);
+        return from_hip(ce, "upload of the natural-order map");
+    }
+    g_nat.emplace(key, mem);
+    out = static_cast<const int32_t *>(mem);
+    return TRA_OK;
+}
+
+// Checks shared by the natural-order attention entry points (after check_attn_common).
+tra_status check_natural(int F, int H, int W, int D, tra_dtype dt, int tile_h, int tile_w, TileGeom &g) {
+    const tra_status st = check_grid(F, H, W, tile_h, tile_w, g);
+    if (st != TRA_OK) return st;
+    if (dt != TRA_BF16 || D != 128) return TRA_ERR_UNSUPPORTED;
+    if (W % 4 != 0 || tile_w % 4 != 0) return TRA_ERR_UNSUPPORTED;
+    if ((int64_t)g.N * D * 2 > (int64_t)0xFFFFFFFF) return TRA_ERR_UNSUPPORTED;  // 32-bit row offsets per head
+    return TRA_OK;
+}
+
 tra_status check_mask_args(int F, int H, int W, float tau, float gamma, int block_q, int block_k, int tile_h,
                            int tile_w, TileGeom &g) {
     const tra_status st = check_grid(F, H, W, tile_h, tile_w, g);
@@ -375,6 +437,47 @@ tra_status tra_dense_attn_entropy_mask(const void *q, const void *k, const void 
     const tra::AttnArgs a = attn_args(q, k, v, o, entropy, lse, outer, g.N, sm_scale);
     clear_pending_error();
     return from_hip(tra::launch_dense_mask(a, m, s), "dense attention with mask");
+}
+
+tra_status tra_dense_attn_entropy_natural(const void *q, const void *k, const void *v, void *o, float *entropy,
+                                          float *lse, int outer, int F, int H, int W, int D, tra_dtype dt,
+                                          float sm_scale, int tile_h, int tile_w, hipStream_t s) {
+    if (F < 1 || H < 1 || W < 1) return TRA_ERR_INVALID_ARG;
+    const int64_t N = (int64_t)F * H * W;
+    if (N > kMaxN) return TRA_ERR_UNSUPPORTED;
+    tra_status st = check_attn_common(q, k, v, o, outer, (int)N, D, dt, sm_scale);
+    if (st != TRA_OK) return st;
+    TileGeom g;
+    st = check_natural(F, H, W, D, dt, tile_h, tile_w, g);
+    if (st != TRA_OK) return st;
+    tra::AttnArgs a = attn_args(q, k, v, o, entropy, lse, outer, g.N, sm_scale);
+    st = get_nat_table(g, a.nat4);
+    if (st != TRA_OK) return st;
+    clear_pending_error();
+    return from_hip(tra::launch_attention_natural(a, false, s), "dense attention (natural order)");
+}
+
+tra_status tra_block_sparse_attn_natural(const void *q, const void *k, const void *v, void *o, float *lse,
+                                         const int32_t *kv_count, const int32_t *kv_index, int outer, int F, int H,
+                                         int W, int D, tra_dtype dt, float sm_scale, int block_q, int block_k,
+                                         int tile_h, int tile_w, hipStream_t s) {
+    if (F < 1 || H < 1 || W < 1) return TRA_ERR_INVALID_ARG;
+    const int64_t N = (int64_t)F * H * W;
+    if (N > kMaxN) return TRA_ERR_UNSUPPORTED;
+    tra_status st = check_attn_common(q, k, v, o, outer, (int)N, D, dt, sm_scale);
+    if (st != TRA_OK) return st;
+    if (!kv_count || !kv_index) return TRA_ERR_INVALID_ARG;
+    if (block_q < 1 || block_k < 1) return TRA_ERR_INVALID_ARG;
+    if (block_q != 128 || block_k != 64) return TRA_ERR_UNSUPPORTED;
+    TileGeom g;
+    st = check_natural(F, H, W, D, dt, tile_h, tile_w, g);
+    if (st != TRA_OK) return st;
+    tra::AttnArgs a = attn_args(q, k, v, o, nullptr, lse, outer, g.N, sm_scale);
+    a.kv_count = kv_count; a.kv_index = kv_index;
+    st = get_nat_table(g, a.nat4);
+    if (st != TRA_OK) return st;
+    clear_pending_error();
+    return from_hip(tra::launch_attention_natural(a, true, s), "sparse attention (natural order)");
 }
 
 tra_status tra_block_sparse_attn(const void *q, const void *k, const void *v, void *o, float *lse,

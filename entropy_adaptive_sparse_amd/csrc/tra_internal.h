@@ -87,10 +87,17 @@ struct AttnArgs {
     int outer, N, nqb, nkb;
     float c;          // sm_scale * log2(e)
     float sm_scale;
+    // null: q, k, v, o in tile-major order.  Otherwise they are in natural order and
+    // nat4[g] is the natural row of tile-major position 4 g (every aligned group of four
+    // tile-major positions is a run of four natural rows); entropy and lse stay tile-major.
+    const int32_t *nat4;
 };
 
 // dtype: 0 = fp32, 1 = bf16.  sparse: walk kv_index; else every k-block (dense).
 hipError_t launch_attention(const AttnArgs &a, int D, int dtype, int block_q, bool sparse, hipStream_t s);
+
+// natural-order q, k, v, o (a.nat4 set): bf16, D = 128; sparse with 128-query blocks
+hipError_t launch_attention_natural(const AttnArgs &a, bool sparse, hipStream_t s);
 
 // dense attention + entropy with the mask builder as epilogue (bf16, D = 128, block_q = 128)
 hipError_t launch_dense_mask(const AttnArgs &a, const MaskArgs &m, hipStream_t s);

@@ -26,9 +26,11 @@
  *    nothing.  A failing HIP call returns TRA_ERR_HIP.  No C++ exception
  *    crosses the ABI.
  *  - Library state: a per-device cache of small fp64 tables and block
- *    geometry for tra_build_block_mask, guarded by a mutex.  Its first use for
- *    a geometry allocates and uploads them synchronously (tra_mask_prepare
- *    does that ahead of time); entries live until the process ends.
+ *    geometry for tra_build_block_mask, and of the tile-major map for the
+ *    natural-order attention calls, guarded by a mutex.  Its first use for a
+ *    geometry allocates and uploads them synchronously (tra_mask_prepare
+ *    does that ahead of time for the mask); entries live until the process
+ *    ends.
  */
 #ifndef TRA_H_
 #define TRA_H_
@@ -182,6 +184,36 @@ tra_status tra_dense_attn_entropy_mask(const void *q, const void *k, const void 
                                        int vote_threshold, int tile_h, int tile_w, int32_t *kv_count,
                                        int32_t *kv_index, int64_t kv_index_capacity, uint8_t *block_mask,
                                        hipStream_t s);
+
+/*
+ * The two attention passes on NATURAL-order tensors, with the tile-major
+ * permutation folded into their loads and stores (pipeline step 3: the
+ * tile-major layout keeps spatial neighbours contiguous; here it is applied
+ * while the kernels copy rows, so no permuted copy of q, k, v or o exists).
+ *
+ * Results equal, bit for bit,
+ *   tra_tile_major_permute of q, k, v; the tile-major call; and
+ *   tra_tile_major_unpermute of o,
+ * for the same tile_h, tile_w: o is written in natural order, while entropy
+ * and lse (each may be NULL) stay indexed by TILE-MAJOR position, the order
+ * tra_build_block_mask reads, and kv_count / kv_index are the tile-major
+ * block lists tra_build_block_mask writes.
+ *
+ * q, k, v, o: device, [outer][N][128] bf16, natural order, N = F*H*W.
+ * Supported: bf16, D = 128, W and tile_w multiples of 4 (then every aligned
+ * group of four tile-major positions is a run of four natural rows), N*D*2 <
+ * 2^32; sparse: block_q = 128, block_k = 64.  Anything else returns
+ * TRA_ERR_UNSUPPORTED before any HIP call.  The first call for a geometry
+ * builds and uploads the map (N/4 int32 natural row indices) synchronously;
+ * it stays in the per-device cache until the process ends.
+ */
+tra_status tra_dense_attn_entropy_natural(const void *q, const void *k, const void *v, void *o, float *entropy,
+                                          float *lse, int outer, int F, int H, int W, int D, tra_dtype dt,
+                                          float sm_scale, int tile_h, int tile_w, hipStream_t s);
+tra_status tra_block_sparse_attn_natural(const void *q, const void *k, const void *v, void *o, float *lse,
+                                         const int32_t *kv_count, const int32_t *kv_index, int outer, int F, int H,
+                                         int W, int D, tra_dtype dt, float sm_scale, int block_q, int block_k,
+                                         int tile_h, int tile_w, hipStream_t s);
 
 #ifdef __cplusplus
 }

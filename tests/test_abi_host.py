@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
               "tra_build_block_mask", "tra_block_sparse_attn", "tra_mask_prepare", "tra_status_string",
-              "tra_dense_attn_entropy_mask"):
+              "tra_dense_attn_entropy_mask", "tra_dense_attn_entropy_natural", "tra_block_sparse_attn_natural"):
         assert n in names
 
 
@@ -151,3 +151,37 @@ def test_fused_warmup_validation(lib):
     assert call(a16=32) == UNSUPPORTED                       # block_k
     assert call(a7=65, a8=8, a9=8) == UNSUPPORTED            # more frames than the tile buffers hold
     assert call(a22=2 * 8 * 16 - 1) == CAPACITY              # kv_index capacity
+
+
+def test_natural_order_validation(lib):
+    fd = lib.tra_dense_attn_entropy_natural
+    # q k v o H lse outer F H W D dt scale th tw stream
+    dense = [FAKE, FAKE2, FAKE3, FAKE4, None, None, 2, 4, 16, 16, 128, BF16, 0.088, 8, 8, None]
+    fs = lib.tra_block_sparse_attn_natural
+    # q k v o lse cnt idx outer F H W D dt scale bq bk th tw stream
+    sparse = [FAKE, FAKE2, FAKE3, FAKE4, None, FAKE + 64, FAKE2 + 64, 2, 4, 16, 16, 128, BF16, 0.088, 128, 64, 8, 8,
+              None]
+
+    def call(f, base, **kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    for f, base in ((fd, dense), (fs, sparse)):
+        assert call(f, base, a0=None) == INVALID                  # q
+        assert call(f, base, a3=FAKE2) == INVALID                 # o aliases k
+    assert call(fd, dense, a6=0) == INVALID                       # outer
+    assert call(fd, dense, a7=0) == INVALID                       # F
+    assert call(fs, sparse, a7=0) == INVALID                      # outer
+    assert call(fs, sparse, a8=0) == INVALID                      # F
+    assert call(fd, dense, a9=18) == UNSUPPORTED                  # W not a multiple of 4
+    assert call(fd, dense, a14=6) == UNSUPPORTED                  # tile width not a multiple of 4
+    assert call(fd, dense, a10=64) == UNSUPPORTED                 # D = 64
+    assert call(fd, dense, a11=F32) == UNSUPPORTED                # fp32
+    assert call(fd, dense, a13=0) == INVALID                      # tile height
+    assert call(fs, sparse, a5=None) == INVALID                   # kv_count
+    assert call(fs, sparse, a6=None) == INVALID                   # kv_index
+    assert call(fs, sparse, a14=64) == UNSUPPORTED                # block_q = 64
+    assert call(fs, sparse, a15=32) == UNSUPPORTED                # block_k
+    assert call(fs, sparse, a10=18) == UNSUPPORTED                # W not a multiple of 4
+    assert call(fs, sparse, a12=F32) == UNSUPPORTED               # fp32

@@ -1,0 +1,121 @@
+"""GPU: the natural-order attention calls (the tile-major permutation of "Token Radius
+Attention for Efficient Video Generation", section 2, TRA pipeline step 3, applied inside
+the kernels' loads and stores) equal the permute -> tile-major call -> unpermute chain bit
+for bit, and the oracle within the attention tolerances.
+
+The tile-major calls are pinned to the oracle in test_gpu_attention.py; here the natural
+calls are compared with them on the same inputs (o in natural order, entropy and lse by
+tile-major position), plus one direct oracle check in natural order.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from entropy_adaptive_sparse_amd import workloads
+from gpu_util import check_output, device, qkv_inputs, say, small_workload, torch_mod, tra
+
+pytestmark = pytest.mark.gpu
+
+
+def _wl(seed, F, H, W, tile=(8, 8), tau=0.03, outer=2):
+    wl = small_workload(seed, F, H, W, 128, "bf16", outer=outer, tau=tau)
+    return dataclasses.replace(wl, tile_h=tile[0], tile_w=tile[1])
+
+
+def _bits(x):
+    torch = torch_mod()
+    return x.view(torch.int16) if x.dtype == torch.bfloat16 else x
+
+
+def _compare(t, wl, q, k, v):
+    """natural calls vs the permuted chain; returns the natural dense outputs and the lists"""
+    torch = torch_mod()
+    F, H, W, th, tw = wl.F, wl.H, wl.W, wl.tile_h, wl.tile_w
+    qp, kp, vp = (t.tile_major_permute(x, F, H, W, th, tw) for x in (q, k, v))
+    o1, h1, l1 = t.dense_attn_entropy(qp, kp, vp, wl.sm_scale, entropy=True, lse=True)
+    o1n = t.tile_major_unpermute(o1, F, H, W, th, tw)
+    o2, h2, l2 = t.dense_attn_entropy_natural(q, k, v, F, H, W, wl.sm_scale, entropy=True, lse=True, tile_h=th,
+                                              tile_w=tw)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(o1n), _bits(o2)), "dense o"
+    assert torch.equal(h1, h2), "entropy"
+    assert torch.equal(l1, l2), "lse"
+    # entropy off: the kernel without the entropy sums
+    o3, _, _ = t.dense_attn_entropy(qp, kp, vp, wl.sm_scale, entropy=False)
+    o4, _, _ = t.dense_attn_entropy_natural(q, k, v, F, H, W, wl.sm_scale, entropy=False, tile_h=th, tile_w=tw)
+    assert torch.equal(_bits(t.tile_major_unpermute(o3, F, H, W, th, tw)), _bits(o4)), "dense o (no entropy)"
+
+    cnt, idx, _ = t.build_block_mask(h1, F, H, W, wl.tau, wl.gamma, wl.block_q, wl.block_k, wl.vote_threshold,
+                                     th, tw)
+    s1, sl1 = t.block_sparse_attn(qp, kp, vp, cnt, idx, wl.block_q, wl.block_k, wl.sm_scale, lse=True)
+    s2, sl2 = t.block_sparse_attn_natural(q, k, v, cnt, idx, F, H, W, wl.block_q, wl.block_k, wl.sm_scale, lse=True,
+                                          tile_h=th, tile_w=tw)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(t.tile_major_unpermute(s1, F, H, W, th, tw)), _bits(s2)), "sparse o"
+    assert torch.equal(sl1, sl2), "sparse lse"
+    say("  block density %.3f" % float(cnt.float().sum().item() / (cnt.shape[0] * cnt.shape[1] * idx.shape[2])))
+    return o2, h2
+
+
+@pytest.mark.parametrize("F,H,W,tile", [
+    (4, 16, 16, (8, 8)),
+    (3, 15, 20, (8, 8)),      # N = 900: ragged last q- and k-block; clipped tiles 7 x 8 and 7 x 4
+    (2, 45, 80, (8, 8)),      # one 720p latent frame pair: 5-row edge tiles, k-blocks straddling tiles
+    (5, 30, 52, (8, 8)),      # 480p-like rows: 4-wide edge tiles
+    (3, 21, 24, (6, 12)),     # other tile shapes
+    (2, 9, 28, (4, 4)),
+])
+def test_natural_equals_permuted_chain(F, H, W, tile):
+    t = tra()
+    wl = _wl(300 + F + H + W, F, H, W, tile)
+    say("natural order", F, H, W, tile)
+    q, k, v = (x.to(device()) for x in qkv_inputs(wl))
+    _compare(t, wl, q, k, v)
+
+
+def test_natural_against_oracle(orc):
+    t = tra()
+    wl = _wl(333, 3, 15, 20)
+    say("natural order vs oracle", wl.F, wl.H, wl.W)
+    qc, kc, vc = qkv_inputs(wl)
+    o, ent = _compare(t, wl, qc.to(device()), kc.to(device()), vc.to(device()))
+    o = o.float().cpu().numpy()
+    ent = ent.cpu().numpy()
+    perm = orc.tile_major_order(wl.F, wl.H, wl.W)
+    for h in range(wl.outer):
+        ro, rH, _ = orc.attention(*(x[h].float().numpy().astype(np.float64) for x in (qc, kc, vc)), wl.sm_scale)
+        check_output(o[h], ro, "bf16")                              # natural order
+        assert float(np.max(np.abs(ent[h] - rH[perm]))) <= 1e-3      # tile-major order
+
+
+def test_natural_full_size_workload3():
+    torch = torch_mod()
+    t = tra()
+    wl = workloads.get(3)
+    say("natural order at full size", wl.name)
+    q, k, v = (x.to(device()) for x in qkv_inputs(wl))
+    F, H, W = wl.F, wl.H, wl.W
+    qp, kp, vp = (t.tile_major_permute(x, F, H, W) for x in (q, k, v))
+    o1, h1, _ = t.dense_attn_entropy(qp, kp, vp, wl.sm_scale, entropy=True)
+    cnt, idx, _ = t.build_block_mask(h1, F, H, W, wl.tau, wl.gamma, wl.block_q, wl.block_k, wl.vote_threshold)
+    s1, _ = t.block_sparse_attn(qp, kp, vp, cnt, idx, wl.block_q, wl.block_k, wl.sm_scale, out=o1)
+    del qp, kp, vp
+    s1n = t.tile_major_unpermute(s1, F, H, W)
+    del s1
+    s2, _ = t.block_sparse_attn_natural(q, k, v, cnt, idx, F, H, W, wl.block_q, wl.block_k, wl.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(s1n), _bits(s2)), "sparse o at full size"
+    del s1n, s2
+    d2, h2, _ = t.dense_attn_entropy_natural(q, k, v, F, H, W, wl.sm_scale, entropy=True)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2), "entropy at full size"
+
+
+def test_natural_rejects_unsupported():
+    torch = torch_mod()
+    t = tra()
+    q = torch.zeros((1, 2 * 6 * 18, 128), dtype=torch.bfloat16, device=device())
+    with pytest.raises(t.TraError) as ei:
+        t.dense_attn_entropy_natural(q, q.clone(), q.clone(), 2, 6, 18)   # W = 18
+    assert ei.value.code == 2
