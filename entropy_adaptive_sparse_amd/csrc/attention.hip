@@ -8,8 +8,9 @@
 // section 3 contribution 3 (entropy fused into the attention kernel).
 //
 // Both modes share one tile engine (bf16 inputs, fp32 accumulation).  A workgroup owns
-// one q-block; each wavefront owns 32 queries and walks 64-key tiles: every k-block in
-// order (dense) or the k-blocks listed in kv_index (sparse).  Per tile and wavefront:
+// one q-block (sparse; two for dense, 8 wavefronts, so each staged tile serves twice the
+// queries); each wavefront owns 32 queries and walks 64-key tiles: every k-block in order
+// (dense) or the k-blocks listed in kv_index (sparse).  Per tile and wavefront:
 //   S^T = K Q^T      on MFMA (v_mfma_f32_32x32x16_bf16), K from LDS, Q^T in registers,
 //                    so a lane owns one query and 32 of the tile's keys;
 //   softmax          in base 2 with a lazily moved running max (it only moves when a
@@ -27,7 +28,10 @@
 // barrier per tile.  Workgroups are ordered so that the 8 XCDs work through the same
 // heads together, each on runs of neighbouring q-blocks.  The warm-up variant
 // attn_mask_kernel ends with the mask builder (mask_impl.h) for its own q-block, run in
-// the freed tile buffers (TRA pipeline steps 2-3 fused into the entropy pass).
+// the freed tile buffers (TRA pipeline steps 2-3 fused into the entropy pass).  The NAT
+// instantiations read natural-order q, k, v and write natural-order o through the
+// tile-major map (pipeline step 3's layout applied inside the copies), bit for bit the
+// results of the tile-major kernels on permuted tensors.
 #include "mask_impl.h"
 #include "tra_internal.h"
 
@@ -615,8 +619,12 @@ struct MaskEpilogue {
     }
 };
 
+// Two wavefronts per SIMD for the 4-wavefront workgroups (two workgroups per CU); the
+// 8-wavefront ones get two per SIMD from a single workgroup, and the 2-wavefront ones
+// (64-query blocks) are held to one per SIMD by their 64 KB of LDS anyway, so those
+// two take the whole register file.
 template <int D, int NW, int QW, bool SPARSE, bool ENT, bool NAT = false>
-__global__ __launch_bounds__(NW * 64, (QW == 1 && NW <= 4) ? 2 : 1) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, (QW == 1 && NW == 4) ? 2 : 1) void attn_bf16_kernel(AttnArgs a) {
     Bf16Kernel<D, NW, QW, SPARSE, ENT, NAT>::run(a);
 }
 
@@ -762,13 +770,15 @@ hipError_t launch_d(const AttnArgs &a, int dtype, bool sparse, hipStream_t s) {
         if (sparse) return launch_bf16<D, NW, true, false>(a, blocks, s);
         if (ent) return launch_bf16<D, NW, false, true>(a, blocks, s);
         return launch_bf16<D, NW, false, false>(a, blocks, s);
-    } else {
+    } else if constexpr (NW <= 4) {  // the fp32 kernels run 2 or 4 wavefronts
         if (sparse)
             attn_f32_kernel<D, NW, true, false><<<blocks, NW * 64, 0, s>>>(a);
         else if (ent)
             attn_f32_kernel<D, NW, false, true><<<blocks, NW * 64, 0, s>>>(a);
         else
             attn_f32_kernel<D, NW, false, false><<<blocks, NW * 64, 0, s>>>(a);
+    } else {
+        return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
