@@ -185,3 +185,20 @@ def test_natural_order_validation(lib):
     assert call(fs, sparse, a15=32) == UNSUPPORTED                # block_k
     assert call(fs, sparse, a10=18) == UNSUPPORTED                # W not a multiple of 4
     assert call(fs, sparse, a12=F32) == UNSUPPORTED               # fp32
+
+
+def test_header_is_plain_c(tmp_path):
+    # the ABI header compiles as C99 and as C++17 on its own (the HIP runtime API header
+    # supplies hipStream_t; no HIP compiler involved)
+    import shutil
+    import subprocess
+    inc = "/opt/rocm/include"
+    if shutil.which("gcc") is None or not os.path.exists(os.path.join(inc, "hip", "hip_runtime_api.h")):
+        pytest.skip("gcc or the ROCm headers are not available")
+    src = tmp_path / "use.c"
+    src.write_text('#include "tra.h"\nint main(void) { return (int)TRA_OK + (tra_status_string(TRA_OK) == 0); }\n')
+    for cc, std in (("gcc", "-std=c99"), ("g++", "-std=c++17")):
+        lang = ["-x", "c++"] if cc == "g++" else []
+        r = subprocess.run([cc, std, *lang, "-D__HIP_PLATFORM_AMD__", "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
+                            "-I", os.path.join(ROOT, "include"), "-I", inc, str(src)], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr

@@ -65,6 +65,8 @@ def _compare(t, wl, q, k, v):
     (5, 30, 52, (8, 8)),      # 480p-like rows: 4-wide edge tiles
     (3, 21, 24, (6, 12)),     # other tile shapes
     (2, 9, 28, (4, 4)),
+    (1, 4, 8, (8, 8)),        # N = 32: one ragged tile
+    (1, 1, 4, (8, 8)),        # N = 4: one run of four rows
 ])
 def test_natural_equals_permuted_chain(F, H, W, tile):
     t = tra()
