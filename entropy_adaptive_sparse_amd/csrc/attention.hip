@@ -602,20 +602,33 @@ struct Bf16Kernel {
     }
 };
 
-// Mask epilogue of the fused warm-up kernel: the q-block's mask row is built as soon as its
+// Mask epilogue of the fused warm-up kernel: each q-block's mask row is built as soon as its
 // entropies are final, in the attention kernel's own LDS ("Token Radius Attention for
 // Efficient Video Generation", section 2, TRA pipeline steps 2-3 fused with the entropy
-// pass of step 1): no launch, and no entropy read back from HBM.
+// pass of step 1): no launch, and no entropy read back from HBM.  The workgroup holds two
+// q-blocks (8 wavefronts, as the dense kernel): wavefronts 0-3 build the row of the first in
+// the four freed tile buffers, wavefronts 4-7 the row of the second in four more, at once.
 template <int RR>
 struct MaskEpilogue {
     const MaskArgs *m;
     __device__ void operator()(lds_char_t *k0, lds_char_t *k1, lds_char_t *v0, lds_char_t *v1, int o, int qb, int qlocal,
                                float hq, bool valid) const {
         using namespace maskdev;
-        const MaskLds<128, true> L((void *)k0, (void *)k1, (void *)v1, (void *)v0, m->g.F, m->nqf_max);
+        __shared__ __attribute__((aligned(1024))) char e0[16384];
+        __shared__ __attribute__((aligned(1024))) char e1[16384];
+        __shared__ __attribute__((aligned(1024))) char e2[16384];
+        __shared__ __attribute__((aligned(1024))) char e3[16384];
+        __shared__ int visits[2];
+        const int half = threadIdx.x >> 8;
+        const int mqb = 2 * qb + half;
+        void *b0 = half ? (void *)e0 : (void *)k0;
+        void *b1 = half ? (void *)e1 : (void *)k1;
+        void *b2 = half ? (void *)e2 : (void *)v1;
+        void *b3 = half ? (void *)e3 : (void *)v0;
+        const MaskLds<128, true> L(b0, b1, b2, b3, m->g.F, m->nqf_max);
         __syncthreads();  // every wavefront is past its last read of the tiles
-        if (valid) L.H[qlocal] = hq;
-        mask_qblock<128, RR, true, true>(*m, L, o, qb);
+        if (valid) L.H[qlocal & 127] = hq;
+        mask_qblock<128, RR, true, true>(*m, L, o, mqb, threadIdx.x & 255, mqb < m->nqb, MaskPair{visits, half});
     }
 };
 
@@ -628,10 +641,11 @@ __global__ __launch_bounds__(NW * 64, (QW == 1 && NW == 4) ? 2 : 1) void attn_bf
     Bf16Kernel<D, NW, QW, SPARSE, ENT, NAT>::run(a);
 }
 
-// dense attention + entropy + mask row, one workgroup per 128-query block (D = 128, bf16)
+// dense attention + entropy + the mask rows of two 128-query blocks per workgroup (D = 128,
+// bf16; 128 KB of LDS, one workgroup per CU)
 template <int RR>
-__global__ __launch_bounds__(256, 2) void attn_mask_kernel(AttnArgs a, MaskArgs m) {
-    Bf16Kernel<128, 4, 1, false, true>::run(a, MaskEpilogue<RR>{&m});
+__global__ __launch_bounds__(512, 1) void attn_mask_kernel(AttnArgs a, MaskArgs m) {
+    Bf16Kernel<128, 8, 1, false, true>::run(a, MaskEpilogue<RR>{&m});
 }
 
 // ----------------------------------------------------------------------------------
@@ -786,13 +800,15 @@ hipError_t launch_d(const AttnArgs &a, int dtype, bool sparse, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_dense_mask(const AttnArgs &a, const MaskArgs &m, hipStream_t s) {
-    const unsigned blocks = (unsigned)((int64_t)a.outer * a.nqb);
+    AttnArgs b = a;
+    b.nqb = (a.N + 255) / 256;  // attention blocks of two mask q-blocks
+    const unsigned blocks = (unsigned)((int64_t)b.outer * b.nqb);
     switch (m.t.rmax) {
-        case 1: attn_mask_kernel<1><<<blocks, 256, 0, s>>>(a, m); break;
-        case 2: attn_mask_kernel<2><<<blocks, 256, 0, s>>>(a, m); break;
-        case 3: attn_mask_kernel<3><<<blocks, 256, 0, s>>>(a, m); break;
-        case 4: attn_mask_kernel<4><<<blocks, 256, 0, s>>>(a, m); break;
-        default: attn_mask_kernel<0><<<blocks, 256, 0, s>>>(a, m); break;
+        case 1: attn_mask_kernel<1><<<blocks, 512, 0, s>>>(b, m); break;
+        case 2: attn_mask_kernel<2><<<blocks, 512, 0, s>>>(b, m); break;
+        case 3: attn_mask_kernel<3><<<blocks, 512, 0, s>>>(b, m); break;
+        case 4: attn_mask_kernel<4><<<blocks, 512, 0, s>>>(b, m); break;
+        default: attn_mask_kernel<0><<<blocks, 512, 0, s>>>(b, m); break;
     }
     return hipGetLastError();
 }

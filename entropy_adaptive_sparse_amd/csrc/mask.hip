@@ -17,7 +17,7 @@ __global__ __launch_bounds__(kThreads) void build_mask_kernel(MaskArgs a) {
     extern __shared__ int4 smem4[];
     const MaskLds<BQ, false> L(smem4, a.g.F, a.nqf_max);
     const int o = blockIdx.x / a.nqb;
-    mask_qblock<BQ, RR, false, false>(a, L, o, blockIdx.x - o * a.nqb);
+    mask_qblock<BQ, RR, false, false>(a, L, o, blockIdx.x - o * a.nqb, threadIdx.x, true, MaskPair{nullptr, 0});
 }
 
 }  // namespace

@@ -238,37 +238,51 @@ __device__ inline int classify(const MaskArgs &a, const MaskLds<BQ, SPLIT> &L, i
     }
 }
 
-// The mask row of q-block qb of head o, by one workgroup of kThreads threads.  FUSED: the
-// q-block's entropies are already in L.H (the caller computed them); otherwise they are read
-// from a.ent.  L.H must not be written between the caller's fill and this call.
+// Two mask rows built at once by one workgroup (the 8-wavefront warm-up kernel): each half
+// of kThreads threads has its own q-block and LDS state, and both halves execute the same
+// barriers -- the chunk loop runs to the larger of the two halves' visit counts, shared
+// through m, and a half without a q-block (past the last one) only takes part in the
+// barriers.  m = null: one row per workgroup.
+struct MaskPair {
+    int *m;    // [2] in LDS: visit count of each half
+    int half;  // this thread's half
+};
+
+// The mask row of q-block qb of head o, by kThreads threads (tid = 0 .. kThreads - 1).
+// FUSED: the q-block's entropies are already in L.H (the caller computed them); otherwise
+// they are read from a.ent.  L.H must not be written between the caller's fill and this
+// call.  active = false: no q-block, barriers only (pair mode).
 template <int BQ, int RR, bool SPLIT, bool FUSED>
-__device__ inline void mask_qblock(const MaskArgs &a, const MaskLds<BQ, SPLIT> &L, int o, int qb) {
+__device__ inline void mask_qblock(const MaskArgs &a, const MaskLds<BQ, SPLIT> &L, int o, int qb, int tid, bool active,
+                                   MaskPair pair) {
     static_assert(BQ == 64 || BQ == 128, "one or two queries per lane");
     constexpr int NG = MaskLds<BQ, SPLIT>::NG;
     const TileGeom &g = a.g;
     const int F = g.F, nkb = a.nkb, N = g.N, QF = a.nqf_max, C = a.chunk;
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q0 = qb * BQ;
-    const int nq = min(BQ, N - q0);
-    const int fa = q0 / g.HW;
-    const int nqf = (q0 + nq - 1) / g.HW - fa + 1;
+    const int nq = active ? min(BQ, N - q0) : 0;
+    const int fa = active ? q0 / g.HW : 0;
+    const int nqf = active ? (q0 + nq - 1) / g.HW - fa + 1 : 0;
     const float *ent = a.ent + (int64_t)o * N;
-    const int64_t row = (int64_t)o * a.nqb + qb;
+    const int64_t row = active ? (int64_t)o * a.nqb + qb : 0;
     int32_t *idx_row = a.kv_index + row * nkb;
-    uint8_t *mrow = a.block_mask ? a.block_mask + row * nkb : nullptr;
+    uint8_t *mrow = (active && a.block_mask) ? a.block_mask + row * nkb : nullptr;
 
-    for (int i = tid; i < QF; i += kThreads) {
-        L.box[4 * i + 0] = INT_MAX; L.box[4 * i + 1] = INT_MIN;
-        L.box[4 * i + 2] = INT_MAX; L.box[4 * i + 3] = INT_MIN;
-        L.Hk[i] = 0u;
+    if (active) {
+        for (int i = tid; i < QF; i += kThreads) {
+            L.box[4 * i + 0] = INT_MAX; L.box[4 * i + 1] = INT_MIN;
+            L.box[4 * i + 2] = INT_MAX; L.box[4 * i + 3] = INT_MIN;
+            L.Hk[i] = 0u;
+        }
+        if (tid < NG) L.gkey[tid] = 0ull;
+        for (int idx = tid; idx < nqf * F; idx += kThreads) L.lam[idx] = a.t.lam[fa * F + idx];
+        if (mrow)
+            for (int kb = tid; kb < nkb; kb += kThreads) mrow[kb] = 0;
     }
-    if (tid < NG) L.gkey[tid] = 0ull;
     if (tid == 0) *L.n = 0;
-    for (int idx = tid; idx < nqf * F; idx += kThreads) L.lam[idx] = a.t.lam[fa * F + idx];
-    if (mrow)
-        for (int kb = tid; kb < nkb; kb += kThreads) mrow[kb] = 0;
     __syncthreads();
 
     // query positions, entropies, per-frame boxes, largest entropies and stars
@@ -291,78 +305,90 @@ __device__ inline void mask_qblock(const MaskArgs &a, const MaskLds<BQ, SPLIT> &
     __syncthreads();
 
     // 1. frame thresholds Tmax[qf][f'], packed boxes, stars
-    for (int idx = tid; idx < nqf * F; idx += kThreads) {
-        const int qf = idx / F;
-        const unsigned k = L.Hk[qf];
-        const double s = k ? (double)key_float(k) + L.lam[idx] : -INFINITY;
-        L.Tm[idx] = threshold_of(s, a.t);
-    }
-    for (int qf = tid; qf < nqf; qf += kThreads) {
-        const int *b = L.box + 4 * qf;
-        L.boxp[2 * qf] = b[0] | (b[2] << 16);
-        L.boxp[2 * qf + 1] = b[1] | (b[3] << 16);
-    }
-    if (tid < NG) {
-        const unsigned long long k = L.gkey[tid];
-        const int i = k ? (int)(unsigned)k : -1;
-        L.star[tid] = i;
-        L.starp[tid] = i >= 0 ? L.qp[i] : 0;
+    if (active) {
+        for (int idx = tid; idx < nqf * F; idx += kThreads) {
+            const int qf = idx / F;
+            const unsigned k = L.Hk[qf];
+            const double s = k ? (double)key_float(k) + L.lam[idx] : -INFINITY;
+            L.Tm[idx] = threshold_of(s, a.t);
+        }
+        for (int qf = tid; qf < nqf; qf += kThreads) {
+            const int *b = L.box + 4 * qf;
+            L.boxp[2 * qf] = b[0] | (b[2] << 16);
+            L.boxp[2 * qf + 1] = b[1] | (b[3] << 16);
+        }
+        if (tid < NG) {
+            const unsigned long long k = L.gkey[tid];
+            const int i = k ? (int)(unsigned)k : -1;
+            L.star[tid] = i;
+            L.starp[tid] = i >= 0 ? L.qp[i] : 0;
+        }
     }
     __syncthreads();
 
-    // 2. per-query thresholds, frame-major so that a wavefront reads one frame's row
-    //    (-1 marks lanes past the end of a ragged q-block: never a hit) ...
-    for (int idx = tid; idx < F * BQ; idx += kThreads) {
-        const int fp = idx / BQ;
-        const int i = idx - fp * BQ;
-        int T = -1;
-        if (i < nq) {
-            const int qf = L.qf[i] - fa;
-            T = 0;
-            if (L.Tm[qf * F + fp] > 0) T = threshold_of((double)L.H[i] + L.lam[qf * F + fp], a.t);
+    if (active) {
+        // 2. per-query thresholds, frame-major so that a wavefront reads one frame's row
+        //    (-1 marks lanes past the end of a ragged q-block: never a hit) ...
+        for (int idx = tid; idx < F * BQ; idx += kThreads) {
+            const int fp = idx / BQ;
+            const int i = idx - fp * BQ;
+            int T = -1;
+            if (i < nq) {
+                const int qf = L.qf[i] - fa;
+                T = 0;
+                if (L.Tm[qf * F + fp] > 0) T = threshold_of((double)L.H[i] + L.lam[qf * F + fp], a.t);
+            }
+            L.Trow(fp)[i] = T;
         }
-        L.Trow(fp)[i] = T;
-    }
-    // ... and the k-block range of each target frame's reach window
-    for (int fp = tid; fp < F; fp += kThreads) {
-        int y0 = INT_MAX, y1 = INT_MIN, x0 = INT_MAX, x1 = INT_MIN;
-        for (int qf = 0; qf < nqf; ++qf) {
-            const int r = isqrt(L.Tm[qf * F + fp]);
-            const int *b = L.box + 4 * qf;
-            y0 = min(y0, b[0] - r); y1 = max(y1, b[1] + r);
-            x0 = min(x0, b[2] - r); x1 = max(x1, b[3] + r);
+        // ... and the k-block range of each target frame's reach window
+        for (int fp = tid; fp < F; fp += kThreads) {
+            int y0 = INT_MAX, y1 = INT_MIN, x0 = INT_MAX, x1 = INT_MIN;
+            for (int qf = 0; qf < nqf; ++qf) {
+                const int r = isqrt(L.Tm[qf * F + fp]);
+                const int *b = L.box + 4 * qf;
+                y0 = min(y0, b[0] - r); y1 = max(y1, b[1] + r);
+                x0 = min(x0, b[2] - r); x1 = max(x1, b[3] + r);
+            }
+            const int ty0 = max(0, y0) / g.th, ty1 = min(g.H - 1, y1) / g.th;
+            const int tx0 = max(0, x0) / g.tw, tx1 = min(g.W - 1, x1) / g.tw;
+            const int ht0 = min(g.th, g.H - ty0 * g.th), ht1 = min(g.th, g.H - ty1 * g.th);
+            const int wt1 = min(g.tw, g.W - tx1 * g.tw);
+            const int first = fp * g.HW + ty0 * g.th * g.W + tx0 * g.tw * ht0;
+            const int last = fp * g.HW + ty1 * g.th * g.W + tx1 * g.tw * ht1 + ht1 * wt1 - 1;
+            L.rlo[fp] = first / a.block_k;
+            L.rhi[fp] = last / a.block_k;
         }
-        const int ty0 = max(0, y0) / g.th, ty1 = min(g.H - 1, y1) / g.th;
-        const int tx0 = max(0, x0) / g.tw, tx1 = min(g.W - 1, x1) / g.tw;
-        const int ht0 = min(g.th, g.H - ty0 * g.th), ht1 = min(g.th, g.H - ty1 * g.th);
-        const int wt1 = min(g.tw, g.W - tx1 * g.tw);
-        const int first = fp * g.HW + ty0 * g.th * g.W + tx0 * g.tw * ht0;
-        const int last = fp * g.HW + ty1 * g.th * g.W + tx1 * g.tw * ht1 + ht1 * wt1 - 1;
-        L.rlo[fp] = first / a.block_k;
-        L.rhi[fp] = last / a.block_k;
     }
     __syncthreads();
 
     // ranges in ascending order: a k-block shared by two frames' ranges is visited
     // once (in the earlier one); each frame sums the visits of the frames before it
-    for (int fp = tid; fp <= F; fp += kThreads) {
-        int pm = -1, acc = 0;
-        for (int j = 0; j < fp; ++j) {
-            const int hi = L.rhi[j];
-            acc += max(0, hi - max(L.rlo[j], pm + 1) + 1);
-            pm = max(pm, hi);
+    if (active) {
+        for (int fp = tid; fp <= F; fp += kThreads) {
+            int pm = -1, acc = 0;
+            for (int j = 0; j < fp; ++j) {
+                const int hi = L.rhi[j];
+                acc += max(0, hi - max(L.rlo[j], pm + 1) + 1);
+                pm = max(pm, hi);
+            }
+            L.rstart[fp] = acc;
+            if (fp < F) L.rfirst[fp] = max(L.rlo[fp], pm + 1);
         }
-        L.rstart[fp] = acc;
-        if (fp < F) L.rfirst[fp] = max(L.rlo[fp], pm + 1);
     }
     __syncthreads();
 
-    const int M = L.rstart[F];
-    const int qp0 = L.qp[min(lane, nq - 1)];
-    const int qp1 = BQ == 128 ? L.qp[min(lane + 64, nq - 1)] : 0;
+    const int M = active ? L.rstart[F] : 0;
+    int Mloop = M;  // chunks to run: this row's, or the larger of the pair's
+    if (pair.m) {
+        if (tid == 0) pair.m[pair.half] = M;
+        __syncthreads();
+        Mloop = max(pair.m[0], pair.m[1]);
+    }
+    const int qp0 = active ? L.qp[min(lane, nq - 1)] : 0;
+    const int qp1 = (active && BQ == 128) ? L.qp[min(lane + 64, nq - 1)] : 0;
     int run = 0;
 
-    for (int base = 0; base < M; base += C) {
+    for (int base = 0; base < Mloop; base += C) {
         // 3a. visit index -> k-block (binary search over the frame ranges); classify
         const int v = base + tid;
         const bool mine = tid < C && v < M;
@@ -429,7 +455,7 @@ __device__ inline void mask_qblock(const MaskArgs &a, const MaskLds<BQ, SPLIT> &
         }
         for (int w = 0; w < kWaves; ++w) run += L.wt[w];
     }
-    if (tid == 0) a.kv_count[row] = run;
+    if (active && tid == 0) a.kv_count[row] = run;
 }
 
 }  // namespace maskdev

@@ -165,8 +165,8 @@ tra_status tra_block_sparse_attn(const void *q, const void *k, const void *v, vo
  * Attention for Efficient Video Generation", section 2, TRA pipeline: the
  * entropy of step 1 feeds the radius mapping and the fused mask kernel of
  * steps 2-3; section 3, the entropy and mask kernels co-designed to keep the
- * overhead small).  A workgroup builds its q-block's mask row as soon as that
- * q-block's entropies are final, in its own on-chip memory.
+ * overhead small).  A workgroup (two 128-query blocks) builds both q-blocks'
+ * mask rows as soon as their entropies are final, in its own on-chip memory.
  *
  * Results equal those of the two separate calls bit for bit: o, entropy and
  * lse as tra_dense_attn_entropy writes them; kv_count, kv_index and

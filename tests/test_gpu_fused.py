@@ -1,6 +1,6 @@
 """GPU: the fused warm-up pass (dense attention + entropy with the mask builder as its
-epilogue, "Token Radius Attention for Efficient Video Generation", section 2, TRA
-pipeline steps 1-3) equals the two separate calls bit for bit.
+epilogue, two q-blocks' rows per workgroup; "Token Radius Attention for Efficient Video
+Generation", section 2, TRA pipeline steps 1-3) equals the two separate calls bit for bit.
 
 The separate calls are pinned to the oracle elsewhere: tra_dense_attn_entropy in
 test_gpu_attention.py (outputs, entropy and lse within tolerance), tra_build_block_mask in
@@ -52,6 +52,9 @@ def _compare(t, wl, q, k, v, vote):
     (40, 2, 3, 0.3, 0.1, 1),         # 6-token frames, 40 frames: thresholds in two LDS buffers
     (2, 45, 80, 0.03, 0.5, 3),
     (6, 30, 52, 0.001, 0.5, 1),
+    (1, 8, 12, 0.05, 0.5, 1),        # one ragged q-block: the workgroup's second half has no row
+    (2, 8, 8, 0.05, 0.5, 2),         # exactly one q-block
+    (3, 7, 9, 0.05, 0.5, 1),         # N = 189: two q-blocks, the second ragged
 ])
 def test_fused_equals_separate(F, H, W, tau, gamma, vote):
     t = tra()
