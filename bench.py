@@ -253,7 +253,7 @@ def main():
 
     # the permutation folded into the attention kernels (natural-order q, k, v, o; same results
     # bit for bit): a reuse step is then one call, a warm-up one dense call plus the mask
-    ms_reuse_nat = ms_dense_nat = None
+    ms_reuse_nat = ms_dense_nat = ms_fused_nat = None
     if wl.dtype == "bf16" and wl.D == 128 and wl.block_q == 128 and wl.W % 4 == 0 and wl.tile_w % 4 == 0:
         def sparse_nat():
             tra.block_sparse_attn_natural(qd, kd, vd, cnt, idx, wl.F, wl.H, wl.W, wl.block_q, wl.block_k,
@@ -277,6 +277,18 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         ms_dense_nat = e0.elapsed_time(e1) / 2
+        if not wl.static_mask:
+            def fused_nat():
+                tra.dense_attn_entropy_mask_natural(qd, kd, vd, wl.F, wl.H, wl.W, tau, wl.gamma, wl.sm_scale,
+                                                    wl.block_q, wl.block_k, wl.vote_threshold, wl.tile_h, wl.tile_w,
+                                                    out=onat, ent_out=ent, kv_count=cnt, kv_index=idx)
+            fused_nat()
+            e0.record()
+            for _ in range(2):
+                fused_nat()
+            e1.record()
+            torch.cuda.synchronize()
+            ms_fused_nat = e0.elapsed_time(e1) / 2
 
     pairs = retained_pairs(torch, cnt, idx, wl.N, wl.block_q, wl.block_k)
     density = pairs / (wl.outer * float(wl.N) ** 2)
@@ -320,6 +332,7 @@ def main():
         "ms_reuse_step": round(ms["permute_qkv"] + ms["sparse_attn"] + ms["unpermute"], 4),
         "ms_reuse_step_natural": None if ms_reuse_nat is None else round(ms_reuse_nat, 4),
         "ms_dense_entropy_natural": None if ms_dense_nat is None else round(ms_dense_nat, 4),
+        "ms_warmup_fused_natural": None if ms_fused_nat is None else round(ms_fused_nat, 4),
         "roofline": {
             "bound": "mfma", "achieved": round(sparse_tf, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(sparse_tf / peak, 4),

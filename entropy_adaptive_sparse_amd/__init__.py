@@ -13,8 +13,8 @@ Functions (names as in the C ABI, without the ``tra_`` prefix):
     dense_attn_entropy_mask (the warm-up pass with the mask builder fused in)
     build_block_mask, mask_prepare
     block_sparse_attn
-    dense_attn_entropy_natural, block_sparse_attn_natural (natural-order q, k, v, o; the
-        tile-major map applied inside the kernels' loads and stores)
+    dense_attn_entropy_natural, dense_attn_entropy_mask_natural, block_sparse_attn_natural
+        (natural-order q, k, v, o; the tile-major map applied inside the kernels' loads and stores)
 """
 from __future__ import annotations
 
@@ -25,7 +25,8 @@ import threading
 __all__ = [
     "TraError", "library_path", "load", "tile_major_permute", "tile_major_unpermute", "dense_attn_entropy",
     "dense_attn_entropy_mask", "build_block_mask", "mask_prepare", "block_sparse_attn",
-    "dense_attn_entropy_natural", "block_sparse_attn_natural", "exported_symbols",
+    "dense_attn_entropy_natural", "dense_attn_entropy_mask_natural", "block_sparse_attn_natural",
+    "exported_symbols",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -77,6 +78,7 @@ def load():
         lib.tra_block_sparse_attn.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, f32, i32, i32, P]
         lib.tra_dense_attn_entropy_mask.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f32, f32, f32,
                                                     i32, i32, i32, i32, i32, P, P, i64, P, P]
+        lib.tra_dense_attn_entropy_mask_natural.argtypes = lib.tra_dense_attn_entropy_mask.argtypes
         lib.tra_dense_attn_entropy_natural.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f32, i32,
                                                        i32, P]
         lib.tra_block_sparse_attn_natural.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f32, i32,
@@ -84,7 +86,7 @@ def load():
         for name in ("tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
                      "tra_build_block_mask", "tra_mask_prepare", "tra_block_sparse_attn",
                      "tra_dense_attn_entropy_mask", "tra_dense_attn_entropy_natural",
-                     "tra_block_sparse_attn_natural"):
+                     "tra_block_sparse_attn_natural", "tra_dense_attn_entropy_mask_natural"):
             getattr(lib, name).restype = i32
         _lib = lib
         return lib
@@ -93,7 +95,7 @@ def load():
 def exported_symbols():
     return ["tra_status_string", "tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
             "tra_build_block_mask", "tra_mask_prepare", "tra_block_sparse_attn", "tra_dense_attn_entropy_mask",
-            "tra_dense_attn_entropy_natural", "tra_block_sparse_attn_natural"]
+            "tra_dense_attn_entropy_natural", "tra_block_sparse_attn_natural", "tra_dense_attn_entropy_mask_natural"]
 
 
 # ------------------------------------------------------------------------------------------------
@@ -193,7 +195,8 @@ def dense_attn_entropy(q, k, v, sm_scale: float | None = None, entropy: bool = T
 def dense_attn_entropy_mask(q, k, v, F: int, H: int, W: int, tau: float, gamma: float, sm_scale: float | None = None,
                             block_q: int = 128, block_k: int = 64, vote_threshold: int = 1, tile_h: int = 8,
                             tile_w: int = 8, entropy: bool = True, lse: bool = False, want_mask: bool = False,
-                            out=None, ent_out=None, lse_out=None, kv_count=None, kv_index=None, block_mask=None):
+                            out=None, ent_out=None, lse_out=None, kv_count=None, kv_index=None, block_mask=None,
+                            _fn="tra_dense_attn_entropy_mask"):
     """Warm-up pass with the mask fused in.  Returns (o, H, lse, kv_count, kv_index, mask); H, lse and
     mask are None unless requested (the mask is built from the entropies either way)."""
     torch = _torch()
@@ -215,10 +218,21 @@ def dense_attn_entropy_mask(q, k, v, F: int, H: int, W: int, tau: float, gamma: 
     if want_mask and msk is None:
         msk = torch.empty((outer, nqb, nkb), dtype=torch.uint8, device=dev)
     scale = (1.0 / D ** 0.5) if sm_scale is None else float(sm_scale)
-    _call("tra_dense_attn_entropy_mask", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(Hh), _ptr(L), outer, F, H, W, D,
+    _call(_fn, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(Hh), _ptr(L), outer, F, H, W, D,
           _dt(q), scale, float(tau), float(gamma), block_q, block_k, int(vote_threshold), tile_h, tile_w, _ptr(cnt),
           _ptr(idx), idx.numel(), _ptr(msk), _stream(q))
     return o, Hh, L, cnt, idx, msk
+
+
+def dense_attn_entropy_mask_natural(q, k, v, F: int, H: int, W: int, tau: float, gamma: float,
+                                    sm_scale: float | None = None, block_q: int = 128, block_k: int = 64,
+                                    vote_threshold: int = 1, tile_h: int = 8, tile_w: int = 8, entropy: bool = True,
+                                    lse: bool = False, want_mask: bool = False, out=None, ent_out=None, lse_out=None,
+                                    kv_count=None, kv_index=None, block_mask=None):
+    """dense_attn_entropy_mask on natural-order q, k, v (o natural; H, lse and the lists tile-major)."""
+    return dense_attn_entropy_mask(q, k, v, F, H, W, tau, gamma, sm_scale, block_q, block_k, vote_threshold, tile_h,
+                                   tile_w, entropy, lse, want_mask, out, ent_out, lse_out, kv_count, kv_index,
+                                   block_mask, _fn="tra_dense_attn_entropy_mask_natural")
 
 
 def mask_prepare(F, H, W, tau, gamma, block_q=128, block_k=64, tile_h=8, tile_w=8) -> None:

@@ -643,9 +643,21 @@ __global__ __launch_bounds__(NW * 64, (QW == 1 && NW == 4) ? 2 : 1) void attn_bf
 
 // dense attention + entropy + the mask rows of two 128-query blocks per workgroup (D = 128,
 // bf16; 128 KB of LDS, one workgroup per CU)
-template <int RR>
+template <int RR, bool NAT>
 __global__ __launch_bounds__(512, 1) void attn_mask_kernel(AttnArgs a, MaskArgs m) {
-    Bf16Kernel<128, 8, 1, false, true>::run(a, MaskEpilogue<RR>{&m});
+    Bf16Kernel<128, 8, 1, false, true, NAT>::run(a, MaskEpilogue<RR>{&m});
+}
+
+template <bool NAT>
+hipError_t launch_dense_mask_t(const AttnArgs &b, const MaskArgs &m, unsigned blocks, hipStream_t s) {
+    switch (m.t.rmax) {
+        case 1: attn_mask_kernel<1, NAT><<<blocks, 512, 0, s>>>(b, m); break;
+        case 2: attn_mask_kernel<2, NAT><<<blocks, 512, 0, s>>>(b, m); break;
+        case 3: attn_mask_kernel<3, NAT><<<blocks, 512, 0, s>>>(b, m); break;
+        case 4: attn_mask_kernel<4, NAT><<<blocks, 512, 0, s>>>(b, m); break;
+        default: attn_mask_kernel<0, NAT><<<blocks, 512, 0, s>>>(b, m); break;
+    }
+    return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------------
@@ -803,14 +815,7 @@ hipError_t launch_dense_mask(const AttnArgs &a, const MaskArgs &m, hipStream_t s
     AttnArgs b = a;
     b.nqb = (a.N + 255) / 256;  // attention blocks of two mask q-blocks
     const unsigned blocks = (unsigned)((int64_t)b.outer * b.nqb);
-    switch (m.t.rmax) {
-        case 1: attn_mask_kernel<1><<<blocks, 512, 0, s>>>(b, m); break;
-        case 2: attn_mask_kernel<2><<<blocks, 512, 0, s>>>(b, m); break;
-        case 3: attn_mask_kernel<3><<<blocks, 512, 0, s>>>(b, m); break;
-        case 4: attn_mask_kernel<4><<<blocks, 512, 0, s>>>(b, m); break;
-        default: attn_mask_kernel<0><<<blocks, 512, 0, s>>>(b, m); break;
-    }
-    return hipGetLastError();
+    return a.nat4 ? launch_dense_mask_t<true>(b, m, blocks, s) : launch_dense_mask_t<false>(b, m, blocks, s);
 }
 
 hipError_t launch_attention_natural(const AttnArgs &a, bool sparse, hipStream_t s) {

@@ -357,6 +357,40 @@ tra::AttnArgs attn_args(const void *q, const void *k, const void *v, void *o, fl
     return a;
 }
 
+// The fused warm-up (dense attention + entropy + mask rows), tile-major or natural-order
+// q, k, v, o.
+tra_status dense_mask_impl(const void *q, const void *k, const void *v, void *o, float *entropy, float *lse, int outer,
+                           int F, int H, int W, int D, tra_dtype dt, float sm_scale, float tau, float gamma,
+                           int block_q, int block_k, int vote_threshold, int tile_h, int tile_w, int32_t *kv_count,
+                           int32_t *kv_index, int64_t kv_index_capacity, uint8_t *block_mask, hipStream_t s,
+                           bool natural) {
+    if (!kv_count || !kv_index || outer < 1 || vote_threshold < 1) return TRA_ERR_INVALID_ARG;
+    TileGeom g;
+    tra_status st = check_mask_args(F, H, W, tau, gamma, block_q, block_k, tile_h, tile_w, g);
+    if (st != TRA_OK) return st;
+    st = check_attn_common(q, k, v, o, outer, g.N, D, dt, sm_scale);
+    if (st != TRA_OK) return st;
+    if (dt != TRA_BF16 || D != 128 || block_q != 128 || block_k != 64) return TRA_ERR_UNSUPPORTED;
+    if (!tra::mask_fits_split(block_q, F, g.HW)) return TRA_ERR_UNSUPPORTED;
+    if (natural) {
+        TileGeom gn;
+        st = check_natural(F, H, W, D, dt, tile_h, tile_w, gn);
+        if (st != TRA_OK) return st;
+    }
+    tra::MaskArgs m;
+    st = fill_mask_args(g, entropy, outer, tau, gamma, block_q, block_k, vote_threshold, kv_count, kv_index,
+                        kv_index_capacity, block_mask, m);
+    if (st != TRA_OK) return st;
+    tra::AttnArgs a = attn_args(q, k, v, o, entropy, lse, outer, g.N, sm_scale);
+    if (natural) {
+        st = get_nat_table(g, a.nat4);
+        if (st != TRA_OK) return st;
+    }
+    clear_pending_error();
+    return from_hip(tra::launch_dense_mask(a, m, s), natural ? "dense attention with mask (natural order)"
+                                                            : "dense attention with mask");
+}
+
 }  // namespace
 
 extern "C" {
@@ -422,21 +456,20 @@ tra_status tra_dense_attn_entropy_mask(const void *q, const void *k, const void 
                                        int vote_threshold, int tile_h, int tile_w, int32_t *kv_count,
                                        int32_t *kv_index, int64_t kv_index_capacity, uint8_t *block_mask,
                                        hipStream_t s) {
-    if (!kv_count || !kv_index || outer < 1 || vote_threshold < 1) return TRA_ERR_INVALID_ARG;
-    TileGeom g;
-    tra_status st = check_mask_args(F, H, W, tau, gamma, block_q, block_k, tile_h, tile_w, g);
-    if (st != TRA_OK) return st;
-    st = check_attn_common(q, k, v, o, outer, g.N, D, dt, sm_scale);
-    if (st != TRA_OK) return st;
-    if (dt != TRA_BF16 || D != 128 || block_q != 128 || block_k != 64) return TRA_ERR_UNSUPPORTED;
-    if (!tra::mask_fits_split(block_q, F, g.HW)) return TRA_ERR_UNSUPPORTED;
-    tra::MaskArgs m;
-    st = fill_mask_args(g, entropy, outer, tau, gamma, block_q, block_k, vote_threshold, kv_count, kv_index,
-                        kv_index_capacity, block_mask, m);
-    if (st != TRA_OK) return st;
-    const tra::AttnArgs a = attn_args(q, k, v, o, entropy, lse, outer, g.N, sm_scale);
-    clear_pending_error();
-    return from_hip(tra::launch_dense_mask(a, m, s), "dense attention with mask");
+    return dense_mask_impl(q, k, v, o, entropy, lse, outer, F, H, W, D, dt, sm_scale, tau, gamma, block_q, block_k,
+                           vote_threshold, tile_h, tile_w, kv_count, kv_index, kv_index_capacity, block_mask, s,
+                           false);
+}
+
+tra_status tra_dense_attn_entropy_mask_natural(const void *q, const void *k, const void *v, void *o, float *entropy,
+                                               float *lse, int outer, int F, int H, int W, int D, tra_dtype dt,
+                                               float sm_scale, float tau, float gamma, int block_q, int block_k,
+                                               int vote_threshold, int tile_h, int tile_w, int32_t *kv_count,
+                                               int32_t *kv_index, int64_t kv_index_capacity, uint8_t *block_mask,
+                                               hipStream_t s) {
+    return dense_mask_impl(q, k, v, o, entropy, lse, outer, F, H, W, D, dt, sm_scale, tau, gamma, block_q, block_k,
+                           vote_threshold, tile_h, tile_w, kv_count, kv_index, kv_index_capacity, block_mask, s,
+                           true);
 }
 
 tra_status tra_dense_attn_entropy_natural(const void *q, const void *k, const void *v, void *o, float *entropy,

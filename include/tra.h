@@ -207,6 +207,18 @@ tra_status tra_dense_attn_entropy_mask(const void *q, const void *k, const void 
  * builds and uploads the map (N/4 int32 natural row indices) synchronously;
  * it stays in the per-device cache until the process ends.
  */
+/*
+ * tra_dense_attn_entropy_mask on natural-order q, k, v, o (the warm-up step in one call):
+ * results equal tra_dense_attn_entropy_mask on the permuted tensors bit for bit, with o
+ * unpermuted; entropy, lse and the block lists are tile-major.  Supported: the intersection
+ * of what the two calls above support.
+ */
+tra_status tra_dense_attn_entropy_mask_natural(const void *q, const void *k, const void *v, void *o, float *entropy,
+                                               float *lse, int outer, int F, int H, int W, int D, tra_dtype dt,
+                                               float sm_scale, float tau, float gamma, int block_q, int block_k,
+                                               int vote_threshold, int tile_h, int tile_w, int32_t *kv_count,
+                                               int32_t *kv_index, int64_t kv_index_capacity, uint8_t *block_mask,
+                                               hipStream_t s);
 tra_status tra_dense_attn_entropy_natural(const void *q, const void *k, const void *v, void *o, float *entropy,
                                           float *lse, int outer, int F, int H, int W, int D, tra_dtype dt,
                                           float sm_scale, int tile_h, int tile_w, hipStream_t s);

@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
               "tra_build_block_mask", "tra_block_sparse_attn", "tra_mask_prepare", "tra_status_string",
-              "tra_dense_attn_entropy_mask", "tra_dense_attn_entropy_natural", "tra_block_sparse_attn_natural"):
+              "tra_dense_attn_entropy_mask", "tra_dense_attn_entropy_natural", "tra_block_sparse_attn_natural",
+              "tra_dense_attn_entropy_mask_natural"):
         assert n in names
 
 
@@ -185,6 +186,17 @@ def test_natural_order_validation(lib):
     assert call(fs, sparse, a15=32) == UNSUPPORTED                # block_k
     assert call(fs, sparse, a10=18) == UNSUPPORTED                # W not a multiple of 4
     assert call(fs, sparse, a12=F32) == UNSUPPORTED               # fp32
+    ff = lib.tra_dense_attn_entropy_mask_natural
+    # q k v o H lse outer F H W D dt scale tau gamma bq bk vote th tw cnt idx cap mask stream
+    fused = [FAKE, FAKE2, FAKE3, FAKE4, None, None, 2, 4, 16, 16, 128, BF16, 0.088, 0.03, 0.5, 128, 64, 1, 8, 8,
+             FAKE + 64, FAKE2 + 64, 2 * 8 * 16, None, None]
+    assert call(ff, fused, a20=None) == INVALID                   # kv_count
+    assert call(ff, fused, a13=0.0) == INVALID                    # tau
+    assert call(ff, fused, a9=18) == UNSUPPORTED                  # W not a multiple of 4
+    assert call(ff, fused, a19=6) == UNSUPPORTED                  # tile width not a multiple of 4
+    assert call(ff, fused, a11=F32) == UNSUPPORTED                # fp32
+    assert call(ff, fused, a7=65, a8=8, a9=8) == UNSUPPORTED      # more frames than the tile buffers hold
+    assert call(ff, fused, a22=2 * 8 * 16 - 1) == CAPACITY        # kv_index capacity
 
 
 def test_header_is_plain_c(tmp_path):

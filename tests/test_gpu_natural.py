@@ -76,6 +76,35 @@ def test_natural_equals_permuted_chain(F, H, W, tile):
     _compare(t, wl, q, k, v)
 
 
+@pytest.mark.parametrize("F,H,W,tile,vote", [
+    (4, 16, 16, (8, 8), 1),
+    (3, 15, 20, (8, 8), 2),   # ragged blocks, clipped tiles
+    (2, 45, 80, (8, 8), 1),   # odd number of q-blocks
+    (3, 21, 24, (6, 12), 1),
+    (1, 4, 8, (8, 8), 1),     # one ragged q-block
+])
+def test_natural_fused_warmup_equals_tile_major(F, H, W, tile, vote):
+    torch = torch_mod()
+    t = tra()
+    wl = _wl(400 + F + H + W, F, H, W, tile)
+    say("natural fused warm-up", F, H, W, tile, vote)
+    q, k, v = (x.to(device()) for x in qkv_inputs(wl))
+    th, tw = tile
+    qp, kp, vp = (t.tile_major_permute(x, F, H, W, th, tw) for x in (q, k, v))
+    args = (F, H, W, wl.tau, wl.gamma, wl.sm_scale, wl.block_q, wl.block_k, vote, th, tw)
+    o1, h1, l1, c1, i1, m1 = t.dense_attn_entropy_mask(qp, kp, vp, *args, lse=True, want_mask=True)
+    o2, h2, l2, c2, i2, m2 = t.dense_attn_entropy_mask_natural(q, k, v, *args, lse=True, want_mask=True)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(t.tile_major_unpermute(o1, F, H, W, th, tw)), _bits(o2)), "o"
+    assert torch.equal(h1, h2) and torch.equal(l1, l2), "entropy / lse"
+    assert torch.equal(c1, c2) and torch.equal(m1, m2), "counts / mask"
+    c = c1.cpu().numpy()
+    a, b = i1.cpu().numpy(), i2.cpu().numpy()
+    for hh in range(c.shape[0]):
+        for qb in range(c.shape[1]):
+            assert np.array_equal(a[hh, qb, :c[hh, qb]], b[hh, qb, :c[hh, qb]]), (hh, qb)
+
+
 def test_natural_against_oracle(orc):
     t = tra()
     wl = _wl(333, 3, 15, 20)
