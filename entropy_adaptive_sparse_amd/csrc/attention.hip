@@ -176,6 +176,20 @@ struct Bf16Cfg {
     static __device__ inline int fV(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
+// v, hidden from the optimiser at this point: a value derived from it is computed here, not
+// hoisted out of the loop into a register of its own.
+__device__ inline int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// A uniform pointer, hidden from the optimiser: kept as the copy's scalar base rather than
+// folded into a 64-bit vector address together with the lane offset.
+__device__ inline const char *uniform_ptr(const char *p) {
+    asm volatile("" : "+s"(p));
+    return p;
+}
+
 // A copy's 32-bit lane offset, zero-extended.  The empty asm hides where the value comes
 // from, so the compiler cannot fold the uniform table offset into a loop-invariant 64-bit
 // vector address; the copy keeps the SGPR-base form: uniform base + this offset.
@@ -193,13 +207,40 @@ __device__ inline int lane_value(int v, int i) {
 #endif
 }
 
-// direct global -> LDS copy of one tile; src: the tile's first byte; the wavefront's
-// slots are the DMA consecutive 64-slot ranges starting at slot 64 * DMA * wave.
-template <int NDMA>
-__device__ inline void dma_tile(const char *__restrict__ src, lds_char_t *dst, const int *soff, int wave) {
+// Copy m of a tile moves its 64 slots 64 m .. 64 m + 63: rows m RPI .. m RPI + RPI - 1 (RPI =
+// rows per copy).  The swizzles are XOR-linear in the row (f(m RPI + r) = f(m RPI) ^ f(r),
+// r < RPI), so a lane's offset in copy m is its offset in copy 0, soff0, with the chunk bits
+// flipped by copy_xor(m), plus m RPI rows (1024 bytes).
+template <int D, int NT, bool ISV>
+__device__ inline int copy_xor(int m) {
+    using C = Bf16Cfg<D, NT>;
+    constexpr int RPI = 64 / C::NCH;
+    return (ISV ? C::fV(m * RPI) : C::fK(m * RPI)) << 4;
+}
+
+// direct global -> LDS copy of one full tile; src: the tile's first byte; the wavefront's
+// copies are DMA consecutive ones starting at copy DMA * wave.
+template <int D, int NT, bool ISV>
+__device__ inline void dma_tile(const char *__restrict__ src, lds_char_t *dst, int soff0, int wave) {
+    using C = Bf16Cfg<D, NT>;
     // a uniform base plus a zero-extended 32-bit lane offset selects the copy's SGPR-base form
     // (no 64-bit address arithmetic per copy), and a uniform wavefront index keeps the LDS
     // destination (M0) in scalar registers
+    const int w = __builtin_amdgcn_readfirstlane(wave);
+    const int s0 = opaque(soff0);  // so that the per-copy offsets are not hoisted into registers
+#pragma unroll
+    for (int i = 0; i < C::DMA; ++i) {
+        const int m = w * C::DMA + i;
+        // the copy's rows as a uniform base (an LDS-DMA instruction offset would move the LDS
+        // destination too), plus the lane offset
+        __builtin_amdgcn_global_load_lds(uniform_ptr(src + m * 1024) + lane_offset(s0 ^ copy_xor<D, NT, ISV>(m)),
+                                         dst + m * 1024, 16, 0, 0);
+    }
+}
+
+// the same with a lane offset per copy (relative to src)
+template <int NDMA>
+__device__ inline void dma_tile_lanes(const char *__restrict__ src, lds_char_t *dst, const int *soff, int wave) {
     const int w = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
     for (int i = 0; i < NDMA; ++i)
@@ -231,32 +272,36 @@ __device__ inline int nat_groups(const int32_t *__restrict__ nat4, int key0, int
 // lane i, and soff[i] is relative to the run.  The ragged tile takes per-lane rows.
 template <int D, int NT, bool ISV, bool NAT>
 __device__ inline void fetch_tile(const char *__restrict__ base, nat_table_t nat4, int natv, int key0, int N,
-                                  lds_char_t *dst, const int *soff, int wave, int lane) {
+                                  lds_char_t *dst, int soff0, int wave, int lane) {
     using C = Bf16Cfg<D, NT>;
     static_assert(!NAT || C::NCH == 16, "one copy instruction covers four rows only for D = 128");
     if (key0 + KT <= N) {
         if constexpr (NAT) {
             const int w = __builtin_amdgcn_readfirstlane(wave);
+            const int s0 = opaque(soff0);
 #pragma unroll
             for (int i = 0; i < C::DMA; ++i) {
                 const int m = w * C::DMA + i;  // this copy's slots of the LDS tile
-                __builtin_amdgcn_global_load_lds(base + lane_offset(lane_value(natv, i) + soff[i]), dst + m * 1024, 16,
-                                                 0, 0);
+                const int off = lane_value(natv, i) + (s0 ^ copy_xor<D, NT, ISV>(m));
+                __builtin_amdgcn_global_load_lds(base + lane_offset(off), dst + m * 1024, 16, 0, 0);
             }
         } else {
-            dma_tile<C::DMA>(base + (int64_t)key0 * C::ROW, dst, soff, wave);
+            dma_tile<D, NT, ISV>(base + (int64_t)key0 * C::ROW, dst, soff0, wave);
         }
     } else {
+        // the ragged tile (once per workgroup at most): offsets computed here rather than kept
+        // in registers across the loop
+        const int ln = NAT ? lane : opaque(lane);
         int so[C::DMA];
 #pragma unroll
         for (int i = 0; i < C::DMA; ++i) {
-            const int sl = (wave * C::DMA + i) * 64 + lane;
+            const int sl = (wave * C::DMA + i) * 64 + ln;
             const int row = sl / C::NCH, p = sl % C::NCH;
             const int swz = (p ^ (ISV ? C::fV(row) : C::fK(row))) << 4;
             const int r = min(row, N - 1 - key0);
             so[i] = (NAT ? natural_row(nat4, key0 + r) : r) * C::ROW + swz;
         }
-        dma_tile<C::DMA>(NAT ? base : base + (int64_t)key0 * C::ROW, dst, so, wave);
+        dma_tile_lanes<C::DMA>(NAT ? base : base + (int64_t)key0 * C::ROW, dst, so, wave);
     }
 }
 
@@ -345,7 +390,7 @@ struct Bf16Kernel {
         float c;
         int koff[D / 16];
         int voff[D / 32];
-        int soffK[C::DMA], soffV[C::DMA];
+        int soffK, soffV;  // lane offset in copy 0 of a K / V tile (copy_xor gives the others)
         bf16x8_t qf[QW][D / 16];
         f32x16_t oacc[D / 32][QW];
         RowState st[QW];
@@ -391,6 +436,10 @@ struct Bf16Kernel {
         }
         // b.
         const float c = x.c;
+        // LLVM's small-GEMM interleave for this block: each matrix instruction followed by two
+        // LDS reads, so the K operands are read ahead of their products (measured: 3% faster
+        // sparse, dense and fused calls than the default schedule)
+        __builtin_amdgcn_iglp_opt(0);
         qk_tile<D, NT, QW>(sn, kn, x.koff, x.qf);
         float nm[QW], ls[QW], ts[QW];
 #pragma unroll
@@ -522,13 +571,12 @@ struct Bf16Kernel {
             for (int db = 0; db < D / 32; ++db)
                 x.voff[db] = row * C::ROW + 64 * (db ^ sel) + 16 * u + 8 * (i & 1);
         }
-#pragma unroll
-        for (int i = 0; i < C::DMA; ++i) {
-            const int sl = (x.wave * C::DMA + i) * 64 + lane;
-            const int row = sl / C::NCH, p = sl % C::NCH;
-            const int rel = NAT ? row & 3 : row;  // NAT: relative to the copy's run of four rows
-            x.soffK[i] = rel * C::ROW + ((p ^ C::fK(row)) << 4);
-            x.soffV[i] = rel * C::ROW + ((p ^ C::fV(row)) << 4);
+        {
+            // copy 0's slots: row lane / NCH, chunk lane % NCH; for NAT the row counts within the
+            // copy's run of four natural rows, which is the same number
+            const int row = lane / C::NCH, p = lane % C::NCH;
+            x.soffK = row * C::ROW + ((p ^ C::fK(row)) << 4);
+            x.soffV = row * C::ROW + ((p ^ C::fV(row)) << 4);
         }
 
         if (SPARSE) {
