@@ -65,9 +65,10 @@ def test_fused_equals_separate(F, H, W, tau, gamma, vote):
     say("  block density", dens)
 
 
-def test_fused_full_size_workload3():
+@pytest.mark.parametrize("wid", [3, 4])  # 4: 33 frames, thresholds in both split buffers
+def test_fused_full_size(wid):
     t = tra()
-    wl = workloads.get(3)
+    wl = workloads.get(wid)
     say("fused warm-up at full size", wl.name)
     q, k, v = _tile_major(t, wl)
     t.mask_prepare(wl.F, wl.H, wl.W, wl.tau, wl.gamma, wl.block_q, wl.block_k)
