@@ -269,7 +269,8 @@ __device__ inline int nat_groups(const int32_t *__restrict__ nat4, int key0, int
 // are fetched from row N - 1 (finite values; their scores are masked later).
 // NAT (D = 128): base holds the rows in natural order.  A copy instruction moves four
 // consecutive tile-major rows, one natural run; natv (nat_groups) holds the run's offset in
-// lane i, and soff[i] is relative to the run.  The ragged tile takes per-lane rows.
+// lane i, and soff0 ^ copy_xor(m) is the lane's offset within the run (copy 0's rows are
+// rows 0-3 of a run).  The ragged tile takes per-lane rows.
 template <int D, int NT, bool ISV, bool NAT>
 __device__ inline void fetch_tile(const char *__restrict__ base, nat_table_t nat4, int natv, int key0, int N,
                                   lds_char_t *dst, int soff0, int wave, int lane) {
