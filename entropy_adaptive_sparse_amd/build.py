@@ -48,6 +48,24 @@ def _compile(src: str) -> str:
     return obj
 
 
+def build_c_check(verbose: bool = False) -> str:
+    """The plain-C caller of the ABI used by the GPU tests (tests/c_abi_check.c), linked
+    against the in-tree libtra.so and the ROCm HIP runtime."""
+    src = os.path.join(ROOT, "tests", "c_abi_check.c")
+    exe = os.path.join(ROOT, "tests", "c_abi_check")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(rocm, "include"), src, "-o", exe, "-L", HERE, "-ltra", "-L", os.path.join(rocm, "lib"),
+           "-lamdhip64", "-lm", "-Wl,-rpath,$ORIGIN/../entropy_adaptive_sparse_amd",
+           "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("c_abi_check build failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
+    if verbose:
+        print("built", exe)
+    return exe
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
@@ -60,6 +78,7 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)
+    build_c_check(verbose)
     return LIB
 
 
