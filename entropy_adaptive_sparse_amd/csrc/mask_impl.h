@@ -46,7 +46,7 @@ namespace tra {
 namespace maskdev {
 
 
-constexpr int kThreads = 256;
+constexpr int kThreads = kMaskThreads;
 constexpr int kWaves = kThreads / 64;
 
 typedef short short2_t __attribute__((ext_vector_type(2)));

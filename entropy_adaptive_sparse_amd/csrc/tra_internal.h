@@ -59,6 +59,8 @@ struct MaskTables {
 
 // Rectangles the mask kernel can hold in LDS for its exact test per chunk of k-blocks.
 constexpr int kMaskEntryCap = 768;
+// Threads of one mask row's builder (a workgroup, or half of the fused kernel's).
+constexpr int kMaskThreads = 256;
 
 struct MaskArgs {
     const float *ent;

@@ -258,6 +258,10 @@ static int orc_geom_init(orc_geom *g, int F, int H, int W, int th, int tw, float
     g->wx = (int32_t *)malloc(sizeof(int32_t) * (size_t)g->N);
     g->lam = (double *)malloc(sizeof(double) * (size_t)F * F);
     g->lnT = (double *)malloc(sizeof(double) * (size_t)(g->tmax + 1));
+    if (!perm || !g->fr || !g->hy || !g->wx || !g->lam || !g->lnT) {
+        free(perm);
+        return 1;
+    }
     orc_tile_major_order(F, H, W, th, tw, perm);
     for (int p = 0; p < g->N; ++p) {
         const int64_t n = perm[p];
@@ -303,7 +307,7 @@ static int orc_is_member_naive(const orc_geom *g, const double *S, float Hi, flo
  * ent: fp32 entropies in tile-major order. */
 int orc_member_row(const float *ent, int F, int H, int W, float tau, float gamma, int th, int tw,
                    int i, uint8_t *member) {
-    orc_geom g;
+    orc_geom g = {0};  /* freed on every exit, also before orc_geom_init runs */
     if (!ent || !member || orc_geom_init(&g, F, H, W, th, tw, tau, gamma)) { orc_geom_free(&g); return 1; }
     if (i < 0 || i >= g.N) { orc_geom_free(&g); return 1; }
     for (int j = 0; j < g.N; ++j) member[j] = (uint8_t)orc_is_member(&g, ent[i], i, j);
@@ -315,7 +319,7 @@ int orc_member_row(const float *ent, int F, int H, int W, float tau, float gamma
  * direct fp64 radius test disagree, over all N*N pairs (tiny grids only). */
 int64_t orc_count_naive_disagreements(const float *ent, int F, int H, int W, float tau, float gamma,
                                       int th, int tw) {
-    orc_geom g;
+    orc_geom g = {0};  /* freed on every exit, also before orc_geom_init runs */
     if (!ent || orc_geom_init(&g, F, H, W, th, tw, tau, gamma)) { orc_geom_free(&g); return -1; }
     double *S = (double *)malloc(sizeof(double) * (size_t)F);
     orc_frame_norm(F, (double)gamma, S);
@@ -383,7 +387,7 @@ static void orc_mask_body(void *vctx, int64_t lo, int64_t hi) {
 int orc_block_mask(const float *ent, int F, int H, int W, float tau, float gamma, int bq, int bk,
                    int vote_threshold, int th, int tw, const int32_t *qblocks, int nsel,
                    uint8_t *mask, int32_t *votes, int nthreads) {
-    orc_geom g;
+    orc_geom g = {0};  /* freed on every exit, also before orc_geom_init runs */
     if (!ent || !qblocks || !mask || !votes || bq < 1 || bk < 1 || vote_threshold < 1 || nsel < 0)
         return 1;
     if (orc_geom_init(&g, F, H, W, th, tw, tau, gamma)) { orc_geom_free(&g); return 1; }
