@@ -144,3 +144,33 @@ def test_mask_capacity_error():
     with pytest.raises(t.TraError) as ei:
         t.build_block_mask(e, 4, 16, 16, 1.0, 0.5, 64, 64, 1, kv_count=cnt, kv_index=idx)
     assert ei.value.code == 4
+
+
+def test_mask_end_to_end_own_entropies(orc):
+    # each side from its own entropies: the GPU's dense pass feeds the GPU mask builder, the
+    # oracle's fp64 entropies (rounded to fp32) feed the oracle's.  Entropies differ within
+    # the 1e-3 nats tolerance, so a query whose disk edge sits on a lattice point can flip a
+    # block: the agreement is a statistic; the bound here only catches a systematic error.
+    torch = torch_mod()
+    t = tra()
+    wl = small_workload(77, 4, 24, 40, 128, "bf16", outer=2, tau=0.03)
+    q, k, v = qkv_inputs(wl)
+    qp, kp, vp = (t.tile_major_permute(x.to(device()), wl.F, wl.H, wl.W) for x in (q, k, v))
+    _, eg, _ = t.dense_attn_entropy(qp, kp, vp, wl.sm_scale, entropy=True)
+    torch.cuda.synchronize()
+    ent_gpu = eg.cpu().numpy()
+    cnt, idx, msk = _gpu_mask(t, ent_gpu, wl.F, wl.H, wl.W, wl.tau, wl.gamma, wl.block_q, wl.block_k, 1)
+    perm = orc.tile_major_order(wl.F, wl.H, wl.W)
+    differ = total = 0
+    worst_ent = 0.0
+    for h in range(wl.outer):
+        _, Hh, _ = orc.attention(q[h].float().numpy(), k[h].float().numpy(), v[h].float().numpy(), wl.sm_scale)
+        ent_orc = Hh[perm].astype(np.float32)
+        worst_ent = max(worst_ent, float(np.max(np.abs(ent_orc - ent_gpu[h]))))
+        ref, _ = orc.block_mask(ent_orc, wl.F, wl.H, wl.W, wl.tau, wl.gamma, wl.block_q, wl.block_k, 1)
+        differ += int(np.sum(ref != msk[h]))
+        total += ref.size
+    say("  entropy max diff %.2e nats; mask entries differing %d of %d (%.3f%%)"
+        % (worst_ent, differ, total, 100.0 * differ / total))
+    assert worst_ent <= 1e-3
+    assert differ <= 0.01 * total
