@@ -192,13 +192,8 @@ def dense_attn_entropy(q, k, v, sm_scale: float | None = None, entropy: bool = T
     return o, H, L
 
 
-def dense_attn_entropy_mask(q, k, v, F: int, H: int, W: int, tau: float, gamma: float, sm_scale: float | None = None,
-                            block_q: int = 128, block_k: int = 64, vote_threshold: int = 1, tile_h: int = 8,
-                            tile_w: int = 8, entropy: bool = True, lse: bool = False, want_mask: bool = False,
-                            out=None, ent_out=None, lse_out=None, kv_count=None, kv_index=None, block_mask=None,
-                            _fn="tra_dense_attn_entropy_mask"):
-    """Warm-up pass with the mask fused in.  Returns (o, H, lse, kv_count, kv_index, mask); H, lse and
-    mask are None unless requested (the mask is built from the entropies either way)."""
+def _dense_mask(fn, q, k, v, F, H, W, tau, gamma, sm_scale, block_q, block_k, vote_threshold, tile_h, tile_w,
+                entropy, lse, want_mask, out, ent_out, lse_out, kv_count, kv_index, block_mask):
     torch = _torch()
     outer, N, D = _check_qkv(q, k, v)
     if N != F * H * W:
@@ -218,10 +213,21 @@ def dense_attn_entropy_mask(q, k, v, F: int, H: int, W: int, tau: float, gamma: 
     if want_mask and msk is None:
         msk = torch.empty((outer, nqb, nkb), dtype=torch.uint8, device=dev)
     scale = (1.0 / D ** 0.5) if sm_scale is None else float(sm_scale)
-    _call(_fn, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(Hh), _ptr(L), outer, F, H, W, D,
+    _call(fn, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(Hh), _ptr(L), outer, F, H, W, D,
           _dt(q), scale, float(tau), float(gamma), block_q, block_k, int(vote_threshold), tile_h, tile_w, _ptr(cnt),
           _ptr(idx), idx.numel(), _ptr(msk), _stream(q))
     return o, Hh, L, cnt, idx, msk
+
+
+def dense_attn_entropy_mask(q, k, v, F: int, H: int, W: int, tau: float, gamma: float, sm_scale: float | None = None,
+                            block_q: int = 128, block_k: int = 64, vote_threshold: int = 1, tile_h: int = 8,
+                            tile_w: int = 8, entropy: bool = True, lse: bool = False, want_mask: bool = False,
+                            out=None, ent_out=None, lse_out=None, kv_count=None, kv_index=None, block_mask=None):
+    """Warm-up pass with the mask fused in.  Returns (o, H, lse, kv_count, kv_index, mask); H, lse and
+    mask are None unless requested (the mask is built from the entropies either way)."""
+    return _dense_mask("tra_dense_attn_entropy_mask", q, k, v, F, H, W, tau, gamma, sm_scale, block_q, block_k,
+                       vote_threshold, tile_h, tile_w, entropy, lse, want_mask, out, ent_out, lse_out, kv_count,
+                       kv_index, block_mask)
 
 
 def dense_attn_entropy_mask_natural(q, k, v, F: int, H: int, W: int, tau: float, gamma: float,
@@ -230,9 +236,9 @@ def dense_attn_entropy_mask_natural(q, k, v, F: int, H: int, W: int, tau: float,
                                     lse: bool = False, want_mask: bool = False, out=None, ent_out=None, lse_out=None,
                                     kv_count=None, kv_index=None, block_mask=None):
     """dense_attn_entropy_mask on natural-order q, k, v (o natural; H, lse and the lists tile-major)."""
-    return dense_attn_entropy_mask(q, k, v, F, H, W, tau, gamma, sm_scale, block_q, block_k, vote_threshold, tile_h,
-                                   tile_w, entropy, lse, want_mask, out, ent_out, lse_out, kv_count, kv_index,
-                                   block_mask, _fn="tra_dense_attn_entropy_mask_natural")
+    return _dense_mask("tra_dense_attn_entropy_mask_natural", q, k, v, F, H, W, tau, gamma, sm_scale, block_q,
+                       block_k, vote_threshold, tile_h, tile_w, entropy, lse, want_mask, out, ent_out, lse_out,
+                       kv_count, kv_index, block_mask)
 
 
 def mask_prepare(F, H, W, tau, gamma, block_q=128, block_k=64, tile_h=8, tile_w=8) -> None:
