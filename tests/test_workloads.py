@@ -36,3 +36,17 @@ def test_density_variants_match_calibration():
             continue
         c = var["%.2f" % d]
         assert tau == c["tau"] and abs(c["density"] - d) < 0.005
+
+
+def test_traffic_profile_is_current():
+    """bench.py reports the sparse kernel's HBM traffic from the committed counter summary only
+    while that summary was taken on the present kernel source; this keeps the two in step."""
+    import importlib.util
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_module", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    src = os.path.join(root, "entropy_adaptive_sparse_amd", "csrc", "attention.hip")
+    traffic = bench.profiled_traffic(workloads.get(3).name, src)
+    assert traffic is not None, "profiles/attn_sparse_hbm_traffic.md was taken on another attention.hip"
+    assert traffic > 3.0e9  # at least q, k, v and o once
