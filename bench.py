@@ -96,8 +96,21 @@ def retained_pairs(torch, cnt, idx, N, bq, bk):
     return float((keys * qsize[None, :]).sum().item())
 
 
-def cpu_baseline(wl, q, k, v, mask_rows, blocks, head, budget_s, perm):
-    """The oracle's masked attention on seeded q-blocks of one head, timed on the host cores."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def cpu_baseline(wl, q, k, v, mask_rows, blocks, head, budget_s, perm, sparse_flops, mask_s):
+    """The oracle's masked attention on seeded q-blocks of one head, timed on the host cores, with
+    the time one whole sparse call (sparse_flops) and one whole mask call would take at the
+    measured rates (mask_s: the oracle's brute-force mask of the same q-blocks)."""
     import numpy as np
     import oracle
 
@@ -118,15 +131,21 @@ def cpu_baseline(wl, q, k, v, mask_rows, blocks, head, budget_s, perm):
             done_pairs += float(len(rows) * (ksz * full[b]).sum())
         passes += 1
     flops = 4.0 * wl.D * done_pairs
+    rate = flops / elapsed
     return {
-        "value": flops / elapsed / 1e12,
+        "value": rate / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
         "sample": "fp64 masked attention of %d seeded q-blocks of head %d (N=%d keys, each q-block's retained "
                   "k-blocks from the oracle's mask) x %d passes: %d query rows, %.3g retained pairs, %.1f s"
                   % (len(blocks), head, wl.N, passes, done_rows, done_pairs, elapsed),
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": cpu_model(),
+        "extrapolated_ms_per_call": round(1e3 * sparse_flops / rate, 1),
+        "mask": {"ms_per_qblock": round(1e3 * mask_s / len(blocks), 3),
+                 "extrapolated_ms_per_call": round(1e3 * mask_s / len(blocks) * wl.outer * wl.nqb, 1),
+                 "sample": "the oracle's brute-force mask rows (every query against every key) of the same %d "
+                           "q-blocks, scaled to %d heads x %d q-blocks" % (len(blocks), wl.outer, wl.nqb)},
     }
 
 
@@ -362,10 +381,13 @@ def main():
         head = 0
         blocks = synth.uniform_ints(7, 64, 0, wl.nqb)
         ent_h = synth.entropy_like(900 + wl.wid, 1, wl.N)[0]
+        t0 = time.perf_counter()
         mask_rows, _ = oracle.block_mask(ent_h, wl.F, wl.H, wl.W, tau, wl.gamma, wl.block_q, wl.block_k,
                                          wl.vote_threshold, qblocks=blocks)
+        mask_s = time.perf_counter() - t0
         print("# cpu baseline ...", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, q, k, v, mask_rows, blocks, head, args.cpu_seconds, perm)
+        result["cpu_baseline"] = cpu_baseline(wl, q, k, v, mask_rows, blocks, head, args.cpu_seconds, perm,
+                                              sparse_flops, mask_s)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
