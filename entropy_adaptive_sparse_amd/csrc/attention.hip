@@ -37,6 +37,8 @@
 
 #include <hip/hip_bf16.h>
 
+#include <type_traits>
+
 namespace tra {
 
 namespace {
@@ -306,11 +308,51 @@ __device__ inline void fetch_tile(const char *__restrict__ base, nat_table_t nat
     }
 }
 
+struct NoCopies {
+    __device__ inline void at(int) const {}
+};
+
+// The K and V tile copies of one step, issued between the S^T products (copy c after product
+// c * NPOS / NC) instead of in one burst at the step's start: a burst holds the wavefront at
+// the vector memory issue path while its matrix instructions wait.  Full tiles only.  The
+// same copies as fetch_tile's: tile-major, ksrc / vsrc are the tiles' first bytes; NAT, they
+// are the head's base and natK / natV hold the tiles' row groups (nat_groups).
+template <int D, int NT, bool NAT>
+struct SpreadCopies {
+    using C = Bf16Cfg<D, NT>;
+    const char *ksrc, *vsrc;
+    lds_char_t *kdst, *vdst;
+    int soffK, soffV, natK, natV, w;
+
+    template <bool ISV>
+    __device__ inline void copy(int i) const {
+        const int m = w * C::DMA + i;
+        const int so = (ISV ? soffV : soffK) ^ copy_xor<D, NT, ISV>(m);
+        lds_char_t *dst = (ISV ? vdst : kdst) + m * 1024;
+        if constexpr (NAT)
+            __builtin_amdgcn_global_load_lds((ISV ? vsrc : ksrc) + lane_offset(lane_value(ISV ? natV : natK, i) + so), dst,
+                                             16, 0, 0);
+        else
+            __builtin_amdgcn_global_load_lds(uniform_ptr((ISV ? vsrc : ksrc) + m * 1024) + lane_offset(so), dst, 16, 0, 0);
+    }
+    __device__ inline void at(int n) const {
+        constexpr int NPOS = 2 * (D / 16), NC = 2 * C::DMA;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            if (c * NPOS / NC == n) {
+                if (c < C::DMA)
+                    copy<false>(c);
+                else
+                    copy<true>(c - C::DMA);
+            }
+    }
+};
+
 // S^T = K Q^T for one 64-key tile and the wavefront's two 32-query blocks: each K operand
-// read from LDS feeds two MFMAs (one per query block).
-template <int D, int NT, int QW>
+// read from LDS feeds two MFMAs (one per query block); cp.at(n) runs after product n.
+template <int D, int NT, int QW, class Copies = NoCopies>
 __device__ inline void qk_tile(f32x16_t (&s)[2][QW], const lds_char_t *kb, const int (&koff)[D / 16],
-                               const bf16x8_t (&qf)[QW][D / 16]) {
+                               const bf16x8_t (&qf)[QW][D / 16], const Copies &cp = Copies()) {
     using C = Bf16Cfg<D, NT>;
     const f32x16_t zero = {};
 #pragma unroll
@@ -322,6 +364,7 @@ __device__ inline void qk_tile(f32x16_t (&s)[2][QW], const lds_char_t *kb, const
 #pragma unroll
             for (int q2 = 0; q2 < QW; ++q2)
                 s[b][q2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[q2][ks], ks == 0 ? zero : s[b][q2], 0, 0, 0);
+            cp.at(b * (D / 16) + ks);
         }
     }
 }
@@ -387,6 +430,7 @@ struct Bf16Kernel {
         nat_table_t nat4;
         const int32_t *nat4v;   // the same table, for vector loads
         int natK, natV;         // nat_groups of the tiles the next K and V copies fetch
+        int keyV, keyK;         // fast sparse steps, tile-major: first keys of tiles j + 1, j + 2
         int N, nkb, ntiles, wave, lane, h;
         float c;
         int koff[D / 16];
@@ -407,17 +451,32 @@ struct Bf16Kernel {
     // V_{j+1}; s: S_j; sn: receives S_{j+1} (computed unconditionally: past the last tile it
     // is unused).  Buffers are distinct LDS objects fixed at compile time, so the reads never
     // wait for the copies in flight.
+    // FAST (j + 3 < ntiles: tiles j + 1 and j + 2 exist and are full, tile j is not the last):
+    // the copies run between the S^T products, and (tile-major) the list entries come a step
+    // ahead in keyV / keyK.  Otherwise the copies are issued at the step's start.
+    template <bool FAST>
     static __device__ inline void step(Ctx &x, int j, lds_char_t *kn, lds_char_t *kd, lds_char_t *vc,
                                        lds_char_t *vd, f32x16_t (&s)[2][QW], f32x16_t (&sn)[2][QW]) {
         int natn = 0;  // NAT: groups of tile j + 3, the K copy of the next step
         if constexpr (NAT) natn = nat_groups<D, NT>(x.nat4v, key0_of(x, min(j + 3, x.ntiles - 1)), x.N, x.wave, x.lane);
-        if (j + 2 < x.ntiles)
-            fetch_tile<D, NT, false, NAT>(x.kp, x.nat4, x.natK, key0_of(x, j + 2), x.N, kd, x.soffK, x.wave, x.lane);
-        if (j + 1 < x.ntiles)
-            fetch_tile<D, NT, true, NAT>(x.vp, x.nat4, x.natV, key0_of(x, j + 1), x.N, vd, x.soffV, x.wave, x.lane);
+        SpreadCopies<D, NT, NAT> cp{};
+        if constexpr (FAST) {
+            const int w = __builtin_amdgcn_readfirstlane(x.wave);
+            if constexpr (NAT)
+                cp = SpreadCopies<D, NT, NAT>{x.kp, x.vp, kd, vd, opaque(x.soffK), opaque(x.soffV), x.natK, x.natV, w};
+            else
+                cp = SpreadCopies<D, NT, NAT>{x.kp + (int64_t)(SPARSE ? x.keyK : key0_of(x, j + 2)) * C::ROW,
+                                              x.vp + (int64_t)(SPARSE ? x.keyV : key0_of(x, j + 1)) * C::ROW, kd, vd,
+                                              opaque(x.soffK), opaque(x.soffV), 0, 0, w};
+        } else {
+            if (j + 2 < x.ntiles)
+                fetch_tile<D, NT, false, NAT>(x.kp, x.nat4, x.natK, key0_of(x, j + 2), x.N, kd, x.soffK, x.wave, x.lane);
+            if (j + 1 < x.ntiles)
+                fetch_tile<D, NT, true, NAT>(x.vp, x.nat4, x.natV, key0_of(x, j + 1), x.N, vd, x.soffV, x.wave, x.lane);
+        }
 
         // a.
-        mask_tail<QW>(s, key0_of(x, j), x.N, x.h);
+        if constexpr (!FAST) mask_tail<QW>(s, key0_of(x, j), x.N, x.h);
         bool move = false;
 #pragma unroll
         for (int q2 = 0; q2 < QW; ++q2) move |= x.mt[q2] > x.st[q2].m + kLazy;
@@ -441,7 +500,10 @@ struct Bf16Kernel {
         // LDS reads, so the K operands are read ahead of their products (measured: 3% faster
         // sparse, dense and fused calls than the default schedule)
         __builtin_amdgcn_iglp_opt(0);
-        qk_tile<D, NT, QW>(sn, kn, x.koff, x.qf);
+        if constexpr (FAST)
+            qk_tile<D, NT, QW>(sn, kn, x.koff, x.qf, cp);
+        else
+            qk_tile<D, NT, QW>(sn, kn, x.koff, x.qf);
         float nm[QW], ls[QW], ts[QW];
 #pragma unroll
         for (int q2 = 0; q2 < QW; ++q2) {
@@ -487,9 +549,26 @@ struct Bf16Kernel {
             x.natV = x.natK;
             x.natK = natn;
         }
-        // this step's copies have landed and every wavefront is done reading
-        wait_dma();
-        __syncthreads();
+        if constexpr (FAST) {
+            if constexpr (SPARSE && !NAT) {
+                // the list entry of tile j + 3 (< ntiles), read while this step's copies land
+                __builtin_amdgcn_sched_barrier(0);
+                x.keyV = x.keyK;
+                x.keyK = key0_of(x, j + 3);
+            }
+            // this step's copies have landed; every wavefront is done reading (each LDS read
+            // of the step has been consumed by its product, and the compiler may not move LDS
+            // accesses across the barrier)
+            wait_dma();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the list entry has arrived
+        } else {
+            // this step's copies have landed and every wavefront is done reading
+            wait_dma();
+            __syncthreads();
+        }
     }
 
     // Epi: called once the outputs are written, with the four (now free) LDS tile buffers,
@@ -614,9 +693,25 @@ struct Bf16Kernel {
 #pragma unroll
             for (int q2 = 0; q2 < QW; ++q2) x.mt[q2] = tile_max<QW>(s0, q2, x.c);
             __syncthreads();  // every wavefront is done with K_0 before K_2 overwrites it
-            for (int j = 0; j < x.ntiles; j += 2) {
-                step(x, j, K1, K0, V0, V1, s0, s1);
-                if (j + 1 < x.ntiles) step(x, j + 1, K0, K1, V1, V0, s1, s0);
+            int j = 0;
+            // The natural-order dense + entropy kernels keep the step-start copies: the spread
+            // ones would push their registers into spilling.
+            if constexpr (!(NAT && ENT)) {
+                if constexpr (SPARSE && !NAT) {
+                    if (x.ntiles > 4) {
+                        x.keyV = key0_of(x, 1);
+                        x.keyK = key0_of(x, 2);
+                    }
+                }
+                // pairs of steps j, j + 1 with j + 4 < ntiles are fast
+                for (; j + 4 < x.ntiles; j += 2) {
+                    step<true>(x, j, K1, K0, V0, V1, s0, s1);
+                    step<true>(x, j + 1, K0, K1, V1, V0, s1, s0);
+                }
+            }
+            for (; j < x.ntiles; j += 2) {
+                step<false>(x, j, K1, K0, V0, V1, s0, s1);
+                if (j + 1 < x.ntiles) step<false>(x, j + 1, K0, K1, V1, V0, s1, s0);
             }
         }
 

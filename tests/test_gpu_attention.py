@@ -196,6 +196,41 @@ def test_sparse_small_full(orc, F, H, W, D, dtype, bq, tau):
     _check_sparse(orc, wl, q2, k2, v2, o2, L2, mask, [0], np.arange(wl.N, dtype=np.int32))
 
 
+@pytest.mark.parametrize("D,dtype,bq", [(128, "bf16", 128), (128, "bf16", 64), (64, "bf16", 128)])
+def test_sparse_every_list_length(orc, D, dtype, bq):
+    # Lists of 0 to 16 k-blocks, with and without the ragged last k-block (N = 1000): the
+    # kernel copies tiles between its products while both tiles of a step's copies are full and
+    # exist (list position + 3 < length), and at the step's start for the last steps; every
+    # length crosses that switch at a different step.
+    wl = small_workload(140 + D + bq, 1, 25, 40, D, dtype, bq=bq)
+    t = tra()
+    say("sparse list lengths", D, dtype, bq)
+    q, k, v = qkv_inputs(wl)
+    rng = np.random.default_rng(11 + D + bq)
+    mask = np.zeros((wl.outer, wl.nqb, wl.nkb), dtype=np.uint8)
+    for h in range(wl.outer):
+        for qb in range(wl.nqb):
+            n = (2 * qb + h) % (wl.nkb + 1)
+            chosen = rng.choice(wl.nkb, size=n, replace=False)
+            if n and (qb + h) % 2:  # half of the lists end with the ragged k-block
+                chosen[0] = wl.nkb - 1
+                chosen = np.unique(chosen)
+                while len(chosen) < n:
+                    chosen = np.unique(np.append(chosen, rng.integers(0, wl.nkb)))
+            mask[h, qb, chosen] = 1
+    cnt, idx = _lists_from_mask(mask)
+    assert set(range(wl.nkb)) <= set(cnt.ravel().tolist())  # lengths 0 .. nkb - 1 at least
+    o, L = _run_sparse(t, wl, q, k, v, cnt, idx)
+    empty = cnt == 0
+    rows = np.array([r for r in range(wl.N) if not empty[0, r // wl.block_q] and not empty[1, r // wl.block_q]],
+                    dtype=np.int32)
+    _check_sparse(orc, wl, q, k, v, o, L, mask, range(wl.outer), rows)
+    for h in range(wl.outer):
+        for qb in np.nonzero(empty[h])[0]:
+            r0, r1 = qb * wl.block_q, min(wl.N, (qb + 1) * wl.block_q)
+            assert float(np.abs(o[h, r0:r1]).max()) == 0.0 and bool(np.isinf(L[h, r0:r1]).all())
+
+
 def test_sparse_all_blocks_equals_dense_bitexact():
     torch = torch_mod()
     t = tra()
