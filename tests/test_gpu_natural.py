@@ -76,6 +76,39 @@ def test_natural_equals_permuted_chain(F, H, W, tile):
     _compare(t, wl, q, k, v)
 
 
+def test_natural_sparse_every_list_length():
+    # lists of 0 to 16 k-blocks, with and without the ragged last k-block (N = 1000): the natural
+    # kernel switches from copies between its products to copies at the step's start at a
+    # different step for every length; it equals the permuted chain bit for bit throughout
+    torch = torch_mod()
+    t = tra()
+    wl = _wl(321, 1, 25, 40)
+    say("natural order, every list length")
+    q, k, v = (x.to(device()) for x in qkv_inputs(wl))
+    rng = np.random.default_rng(17)
+    cnt = np.zeros((wl.outer, wl.nqb), dtype=np.int32)
+    idx = np.full((wl.outer, wl.nqb, wl.nkb), -5, dtype=np.int32)
+    for h in range(wl.outer):
+        for qb in range(wl.nqb):
+            n = (2 * qb + h) % (wl.nkb + 1)
+            chosen = set(rng.choice(wl.nkb, size=n, replace=False).tolist())
+            if n and (qb + h) % 2 and wl.nkb - 1 not in chosen:
+                chosen.discard(min(chosen))
+                chosen.add(wl.nkb - 1)
+            cnt[h, qb] = n
+            idx[h, qb, :n] = sorted(chosen)
+    assert set(range(wl.nkb)) <= set(cnt.ravel().tolist())
+    cnt_d, idx_d = torch.from_numpy(cnt).to(device()), torch.from_numpy(idx).to(device())
+    F, H, W = wl.F, wl.H, wl.W
+    qp, kp, vp = (t.tile_major_permute(x, F, H, W) for x in (q, k, v))
+    s1, l1 = t.block_sparse_attn(qp, kp, vp, cnt_d, idx_d, wl.block_q, wl.block_k, wl.sm_scale, lse=True)
+    s2, l2 = t.block_sparse_attn_natural(q, k, v, cnt_d, idx_d, F, H, W, wl.block_q, wl.block_k, wl.sm_scale,
+                                         lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(t.tile_major_unpermute(s1, F, H, W)), _bits(s2)), "sparse o"
+    assert torch.equal(l1, l2), "sparse lse"
+
+
 @pytest.mark.parametrize("F,H,W,tile,vote", [
     (4, 16, 16, (8, 8), 1),
     (3, 15, 20, (8, 8), 2),   # ragged blocks, clipped tiles
