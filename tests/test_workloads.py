@@ -50,3 +50,13 @@ def test_traffic_profile_is_current():
     traffic = bench.profiled_traffic(workloads.get(3).name, src)
     assert traffic is not None, "profiles/attn_sparse_hbm_traffic.md was taken on another attention.hip"
     assert traffic > 3.0e9  # at least q, k, v and o once
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU and says so for --gpus N > 1 (exit status 2, before any GPU work)."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2 and "one GPU" in (r.stdout + r.stderr)
