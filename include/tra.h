@@ -151,7 +151,9 @@ tra_status tra_mask_prepare(int F, int H, int W, float tau, float gamma, int blo
  * over every token of each retained k-block, nothing else.  q, k, v, o as in
  * tra_dense_attn_entropy (tile-major order); kv_count / kv_index as written
  * by tra_build_block_mask for the same N, block_q, block_k (indices must be
- * in [0, nkb), ascending, counts in [1, nkb]; a row with count 0 yields zeros).
+ * in [0, nkb), ascending, counts in [1, nkb]; a row with count 0 yields zeros
+ * and lse -inf.  Other values are clamped into those ranges, so every access
+ * stays inside q, k, v and the list row, but the result is then unspecified).
  * lse: optional fp32 [outer][N].  With every block retained the result equals
  * tra_dense_attn_entropy's bit for bit (same tile order, same arithmetic).
  */
