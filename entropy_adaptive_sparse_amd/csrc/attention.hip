@@ -37,8 +37,6 @@
 
 #include <hip/hip_bf16.h>
 
-#include <type_traits>
-
 namespace tra {
 
 namespace {

@@ -1,5 +1,6 @@
 """GPU: bench.py keeps its one-line JSON contract (metric, value, roofline with the sparse
-kernel's traffic when the committed counter summary matches the kernel source) on a short run."""
+kernel's traffic, null unless the committed counter summary matches the kernel source) on a
+short run."""
 import json
 import os
 import subprocess
@@ -27,6 +28,8 @@ def test_bench_json_line():
     assert d["unit"] == "TFLOP/s" and d["dtype"] == "bf16" and d["value"] > 0
     rf = d["roofline"]
     assert rf["bound"] == "mfma" and rf["peak"] == 2500.0 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
-    assert isinstance(rf["traffic"], int) and rf["traffic"] > 3.0e9
+    # null while the committed counter summary was taken on another kernel source (the CPU
+    # suite checks that it is current)
+    assert rf["traffic"] is None or (isinstance(rf["traffic"], int) and rf["traffic"] > 3.0e9)
     assert d["config"]["workload"] == "wan2.1-14b-720p-21x45x80"
     assert all(v > 0 for v in d["ms_per_call"].values())
