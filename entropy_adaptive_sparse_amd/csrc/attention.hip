@@ -429,7 +429,7 @@ struct Bf16Kernel {
         const int32_t *nat4v;   // the same table, for vector loads
         int natK, natV;         // nat_groups of the tiles the next K and V copies fetch
         int keyV, keyK;         // fast sparse steps, tile-major: first keys of tiles j + 1, j + 2
-        int N, nkb, ntiles, wave, lane, h;
+        int N, nkb, nfull, ntiles, wave, lane, h;  // nfull: full 64-key tiles, N / 64
         float c;
         int koff[D / 16];
         int voff[D / 32];
@@ -441,7 +441,14 @@ struct Bf16Kernel {
     };
 
     static __device__ inline int key0_of(const Ctx &x, int j) {
-        if (SPARSE) return min(max(x.list[j], 0), x.nkb - 1) * KT;
+        if (SPARSE) return sparse_kblock(x.list[j], x.nkb) * KT;
+        return j * KT;
+    }
+    // the same for the copies between the products, which move whole tiles: an entry naming
+    // the ragged last k-block there (only an invalid list has one before its last entry) is
+    // clamped to the last full one
+    static __device__ inline int key0_full(const Ctx &x, int j) {
+        if (SPARSE) return sparse_full_kblock(x.list[j], x.nfull) * KT;
         return j * KT;
     }
 
@@ -456,15 +463,15 @@ struct Bf16Kernel {
     static __device__ inline void step(Ctx &x, int j, lds_char_t *kn, lds_char_t *kd, lds_char_t *vc,
                                        lds_char_t *vd, f32x16_t (&s)[2][QW], f32x16_t (&sn)[2][QW]) {
         int natn = 0;  // NAT: groups of tile j + 3, the K copy of the next step
-        if constexpr (NAT) natn = nat_groups<D, NT>(x.nat4v, key0_of(x, min(j + 3, x.ntiles - 1)), x.N, x.wave, x.lane);
+        if constexpr (NAT) natn = nat_groups<D, NT>(x.nat4v, key0_full(x, min(j + 3, x.ntiles - 1)), x.N, x.wave, x.lane);
         SpreadCopies<D, NT, NAT> cp{};
         if constexpr (FAST) {
             const int w = __builtin_amdgcn_readfirstlane(x.wave);
             if constexpr (NAT)
                 cp = SpreadCopies<D, NT, NAT>{x.kp, x.vp, kd, vd, opaque(x.soffK), opaque(x.soffV), x.natK, x.natV, w};
             else
-                cp = SpreadCopies<D, NT, NAT>{x.kp + (int64_t)(SPARSE ? x.keyK : key0_of(x, j + 2)) * C::ROW,
-                                              x.vp + (int64_t)(SPARSE ? x.keyV : key0_of(x, j + 1)) * C::ROW, kd, vd,
+                cp = SpreadCopies<D, NT, NAT>{x.kp + (int64_t)(SPARSE ? x.keyK : key0_full(x, j + 2)) * C::ROW,
+                                              x.vp + (int64_t)(SPARSE ? x.keyV : key0_full(x, j + 1)) * C::ROW, kd, vd,
                                               opaque(x.soffK), opaque(x.soffV), 0, 0, w};
         } else {
             if (j + 2 < x.ntiles)
@@ -552,7 +559,7 @@ struct Bf16Kernel {
                 // the list entry of tile j + 3 (< ntiles), read while this step's copies land
                 __builtin_amdgcn_sched_barrier(0);
                 x.keyV = x.keyK;
-                x.keyK = key0_of(x, j + 3);
+                x.keyK = key0_full(x, j + 3);
             }
             // this step's copies have landed; every wavefront is done reading (each LDS read
             // of the step has been consumed by its product, and the compiler may not move LDS
@@ -599,6 +606,7 @@ struct Bf16Kernel {
         const int N = a.N;
         x.N = N;
         x.nkb = a.nkb;
+        x.nfull = N / KT;
         x.c = a.c;
         const int64_t head = (int64_t)o * N * D;
         const __bf16 *qp = static_cast<const __bf16 *>(a.q) + head;
@@ -678,8 +686,8 @@ struct Bf16Kernel {
             int n0 = 0;
             if constexpr (NAT) {
                 n0 = nat_groups<D, NT>(x.nat4v, k0, N, x.wave, lane);
-                x.natV = nat_groups<D, NT>(x.nat4v, key0_of(x, min(1, x.ntiles - 1)), N, x.wave, lane);
-                x.natK = nat_groups<D, NT>(x.nat4v, key0_of(x, min(2, x.ntiles - 1)), N, x.wave, lane);
+                x.natV = nat_groups<D, NT>(x.nat4v, key0_full(x, min(1, x.ntiles - 1)), N, x.wave, lane);
+                x.natK = nat_groups<D, NT>(x.nat4v, key0_full(x, min(2, x.ntiles - 1)), N, x.wave, lane);
             }
             fetch_tile<D, NT, false, NAT>(x.kp, x.nat4, n0, k0, N, K0, x.soffK, x.wave, lane);
             fetch_tile<D, NT, true, NAT>(x.vp, x.nat4, n0, k0, N, V0, x.soffV, x.wave, lane);
@@ -697,11 +705,11 @@ struct Bf16Kernel {
             if constexpr (!(NAT && ENT)) {
                 if constexpr (SPARSE && !NAT) {
                     if (x.ntiles > 4) {
-                        x.keyV = key0_of(x, 1);
-                        x.keyK = key0_of(x, 2);
+                        x.keyV = key0_full(x, 1);
+                        x.keyK = key0_full(x, 2);
                     }
                 }
-                // pairs of steps j, j + 1 with j + 4 < ntiles are fast
+                // pairs of steps j, j + 1 with j + 4 < ntiles are fast (sparse_fast_steps)
                 for (; j + 4 < x.ntiles; j += 2) {
                     step<true>(x, j, K1, K0, V0, V1, s0, s1);
                     step<true>(x, j + 1, K0, K1, V1, V0, s1, s0);
@@ -851,10 +859,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_f32_kernel(AttnArgs a) {
 
     for (int it = 0; it < ntiles; ++it) {
         int kb = it;
-        if (SPARSE) {
-            kb = list[it];
-            if (kb < 0 || kb >= a.nkb) continue;  // uniform across the workgroup
-        }
+        if (SPARSE) kb = sparse_kblock(list[it], a.nkb);  // any entry stays inside k and v
         const int key0 = kb * KT;
         __syncthreads();
         for (int u = tid; u < KT * D; u += NT) {

@@ -81,6 +81,22 @@ size_t mask_lds_bytes(int block_q, int F, int HW);
 bool mask_fits_split(int block_q, int F, int HW);
 
 // ---------------------------------------------------------------- attention
+// Block-sparse attention: the k-block a list entry e names, clamped into [0, nkb), so that any
+// list value keeps every access inside k and v.  The ragged last k-block (N % 64 != 0) is then
+// copied row by row and its rows past N are masked.
+__host__ __device__ inline int sparse_kblock(int e, int nkb) { return min(max(e, 0), nkb - 1); }
+
+// The k-block a copy issued between the S^T products fetches for list entry e.  Those copies
+// move whole 64-row tiles and skip the ragged-tile masking, so the entry is clamped to the last
+// full k-block (nfull = N / 64).  A valid list (ascending, distinct) holds the ragged k-block
+// only as its last entry, which such copies never fetch, so valid lists are unaffected.
+__host__ __device__ inline int sparse_full_kblock(int e, int nfull) { return min(max(e, 0), max(nfull - 1, 0)); }
+
+// Number of leading steps of a sparse list walk of ntiles tiles whose copies run between the
+// products: pairs of steps (j, j + 1) while j + 4 < ntiles.  Step j copies K of tile j + 2 and
+// V of tile j + 1 and reads the list entry of tile j + 3; all are before the last tile.
+__host__ __device__ inline int sparse_fast_steps(int ntiles) { return ntiles > 4 ? 2 * ((ntiles - 3) / 2) : 0; }
+
 struct AttnArgs {
     const void *q, *k, *v;
     void *o;

@@ -78,7 +78,75 @@ hipError_t launch_dense_mask(const AttnArgs &a, const MaskArgs &m, hipStream_t) 
         }                                                 \
     } while (0)
 
+// Bounds model of the block-sparse attention kernel's tile copies.  The kernel walks a list of
+// ntiles entries in steps; step j computes tile j and copies K of tile j + 2 and V of tile j + 1.
+// The first sparse_fast_steps(ntiles) steps issue those copies between their products as whole
+// 64-row tiles (tile-major base + 64 rows) with the list entries taken through
+// sparse_full_kblock; the later steps, and the copies before the first step, go through the
+// row-by-row path, which reads row min(r, N - 1) of the k-block sparse_kblock names.  Every list
+// of every length below, valid or not, must keep each whole-tile copy inside [0, N) and name a
+// k-block in [0, nkb) for the row-by-row path.
+int check_sparse_copy_bounds() {
+    unsigned rng = 12345u;
+    auto next = [&rng]() {
+        rng = rng * 1664525u + 1013904223u;
+        return (int)(rng >> 8);
+    };
+    const int sizes[] = {64, 65, 100, 127, 1000, 1024, 4096 + 16, 75600};
+    for (int N : sizes) {
+        const int nkb = (N + 63) / 64, nfull = N / 64;
+        for (int ntiles = 0; ntiles <= std::min(nkb, 40) + 3; ++ntiles) {
+            const int len = std::min(ntiles, nkb);  // the kernel clamps the count into [0, nkb]
+            for (int trial = 0; trial < 64; ++trial) {
+                std::vector<int> list((size_t)std::max(len, 1));
+                for (int i = 0; i < len; ++i) {
+                    const int kind = next() % 6;
+                    // valid-looking entries, the ragged k-block anywhere, negative and huge values
+                    list[(size_t)i] = kind == 0 ? nkb - 1 : kind == 1 ? -(next() % 100) - 1
+                                    : kind == 2 ? nkb + next() % 1000 : next() % nkb;
+                }
+                const int fast = tra::sparse_fast_steps(len);
+                for (int j = 0; j < len; ++j) {
+                    if (j < fast) {
+                        // K of tile j + 2, V of tile j + 1, the entry of tile j + 3 read ahead
+                        for (int t : {j + 1, j + 2, j + 3}) {
+                            if (t >= len) {
+                                std::fprintf(stderr, "fast step %d of %d reads past the list\n", j, len);
+                                return 1;
+                            }
+                            const int kb = tra::sparse_full_kblock(list[(size_t)t], nfull);
+                            if (kb < 0 || (int64_t)kb * 64 + 64 > N) {
+                                std::fprintf(stderr, "whole-tile copy of k-block %d past N = %d\n", kb, N);
+                                return 1;
+                            }
+                        }
+                    }
+                    const int kb = tra::sparse_kblock(list[(size_t)j], nkb);
+                    if (kb < 0 || kb >= nkb) {
+                        std::fprintf(stderr, "row-by-row copy of k-block %d outside [0, %d)\n", kb, nkb);
+                        return 1;
+                    }
+                }
+                // a valid list (ascending, distinct) never has the ragged k-block before its last entry,
+                // so the whole-tile clamp leaves every entry a fast step fetches unchanged
+                std::vector<int> valid;
+                for (int kb = 0; kb < nkb && (int)valid.size() < len; ++kb)
+                    if (next() % 3 == 0 || nkb - kb <= len - (int)valid.size()) valid.push_back(kb);
+                for (int j = 0; j < fast; ++j)
+                    for (int t : {j + 1, j + 2, j + 3})
+                        if (t < len - 1 && tra::sparse_full_kblock(valid[(size_t)t], nfull) != valid[(size_t)t]) {
+                            std::fprintf(stderr, "clamp changed a valid entry\n");
+                            return 1;
+                        }
+            }
+        }
+    }
+    return 0;
+}
+
 int main() {
+    CHECK(check_sparse_copy_bounds() == 0, "sparse copy bounds");
+
     // mask tables for the workload grids and some ragged ones (host builders run here)
     const int grids[][5] = {{21, 45, 80, 8, 8}, {33, 45, 80, 8, 8}, {21, 30, 52, 8, 8}, {3, 15, 17, 8, 8},
                             {2, 9, 7, 4, 3},    {1, 1, 1, 8, 8},    {40, 2, 3, 8, 8}};
@@ -110,6 +178,9 @@ int main() {
                                             F, H, W, D, TRA_BF16, 0.088f, 128, 64, 8, 8, nullptr) == TRA_OK,
               "sparse natural");
         CHECK(g_attn.nat4 != nullptr, "natural map");
+        CHECK(tra_natural_prepare(F, H, W, 8, 8) == TRA_OK, "natural prepare (cached map)");
+        CHECK(tra_natural_prepare(F, H, 18, 8, 8) == TRA_ERR_UNSUPPORTED, "natural prepare, W = 18");
+        CHECK(tra_natural_prepare(2, 6, 8, 3, 4) == TRA_OK, "natural prepare, new geometry");
         tra::TileGeom g{F, H, W, 8, 8, H * W, N};
         for (int p = 0; p < N; ++p)
             CHECK(g_attn.nat4[p / 4] + p % 4 == tra::tile_major_to_natural(p, g), "natural map entry");
