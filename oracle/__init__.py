@@ -59,6 +59,12 @@ def _load():
             lib.orc_count_naive_disagreements.restype = i64
             lib.orc_block_mask.argtypes = [P, i32, i32, i32, f32, f32, i32, i32, i32, i32, i32, P, i32,
                                            P, P, i32]
+            lib.orc_window_mu.argtypes = [f32]
+            lib.orc_window_mu.restype = f64
+            lib.orc_member_row_1d.argtypes = [P, i32, i32, i32, f32, i32, i32, i32, P]
+            lib.orc_count_naive_disagreements_1d.argtypes = [P, i32, i32, i32, f32, i32, i32]
+            lib.orc_count_naive_disagreements_1d.restype = i64
+            lib.orc_block_mask_1d.argtypes = [P, i32, i32, i32, f32, i32, i32, i32, i32, i32, P, i32, P, P, i32]
             _lib = lib
     return _lib
 
@@ -208,3 +214,47 @@ def mask_to_lists(mask: np.ndarray):
     counts = mask.sum(axis=1).astype(np.int32)
     lists = [np.nonzero(row)[0].astype(np.int32) for row in mask]
     return counts, lists
+
+
+# --------------------------------------------------------------------------------------------
+# 1D-distance variant (section 4, ablation study: the radius mask replaced by a 1D distance):
+# the budget tau * exp(H_i) spent on a window of the natural raster sequence centred on the
+# query, 2 |n_i - n_j| <= K_i
+# --------------------------------------------------------------------------------------------
+def window_mu(tau: float) -> float:
+    """mu = ln tau - ln 2 (fp64): key j is in query i's window iff d = 0 or ln d <= H_i + mu."""
+    return _load().orc_window_mu(float(tau))
+
+
+def member_row_1d(ent: np.ndarray, F, H, W, tau, i, th=8, tw=8) -> np.ndarray:
+    """Window support of the query at tile-major position i: uint8[N] over tile-major key positions."""
+    ent = np.ascontiguousarray(ent, dtype=np.float32)
+    out = np.empty(F * H * W, dtype=np.uint8)
+    _check(_load().orc_member_row_1d(_ptr(ent), F, H, W, float(tau), th, tw, int(i), _ptr(out)), "member_row_1d")
+    return out
+
+
+def naive_disagreements_1d(ent: np.ndarray, F, H, W, tau, th=8, tw=8) -> int:
+    ent = np.ascontiguousarray(ent, dtype=np.float32)
+    n = _load().orc_count_naive_disagreements_1d(_ptr(ent), F, H, W, float(tau), th, tw)
+    if n < 0:
+        raise ValueError("oracle naive_disagreements_1d rejected its arguments")
+    return int(n)
+
+
+def block_mask_1d(ent: np.ndarray, F, H, W, tau, bq, bk, vote_threshold=1, th=8, tw=8, qblocks=None,
+                  nthreads: int | None = None):
+    """Mask rows of the 1D window support for the selected q-blocks of one head (tile-major
+    entropies).  Returns (mask uint8 [S][nkb], votes int32 [S][nkb])."""
+    ent = np.ascontiguousarray(ent, dtype=np.float32)
+    N = F * H * W
+    assert ent.shape == (N,)
+    nqb, nkb = (N + bq - 1) // bq, (N + bk - 1) // bk
+    qblocks = np.arange(nqb, dtype=np.int32) if qblocks is None else np.ascontiguousarray(qblocks, np.int32)
+    S = qblocks.shape[0]
+    mask = np.zeros((S, nkb), dtype=np.uint8)
+    votes = np.zeros((S, nkb), dtype=np.int32)
+    rc = _load().orc_block_mask_1d(_ptr(ent), F, H, W, float(tau), bq, bk, int(vote_threshold), th, tw,
+                                   _ptr(qblocks), S, _ptr(mask), _ptr(votes), nthreads or default_threads())
+    _check(rc, "block_mask_1d")
+    return mask, votes

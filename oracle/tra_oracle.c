@@ -303,6 +303,83 @@ static int orc_is_member_naive(const orc_geom *g, const double *S, float Hi, flo
     return (double)d2 <= rho * rho;
 }
 
+/* ------------------------------------------------------------------------- */
+/* 1D-distance support (section 4, ablation study: the radius mask replaced   */
+/* by a 1D distance).                                                         */
+/*                                                                           */
+/* Reading (the pages name the variant and nothing more): the same token      */
+/* budget K_i = tau * exp(H_i) is spent on a window of the flattened token    */
+/* sequence in its natural raster order n = (f*H + h)*W + w, centred on the   */
+/* query: key j belongs to the support iff                                   */
+/*     2 |n_i - n_j| <= K_i,                                                 */
+/* so the window holds about K_i keys (the 1D counterpart of area matching).  */
+/* No per-frame factor: the 1D sequence has no frame axis.  Canonical        */
+/* evaluation, as for the disk: with d = |n_i - n_j|, j is a member iff       */
+/* d == 0 or ln(d) <= (double)H_i + mu, mu = ln tau - ln 2, ln(d) from a      */
+/* table of ln t for t = 1..N-1 -- the log of the window inequality, fp64,    */
+/* with the C library's log.                                                 */
+/* ------------------------------------------------------------------------- */
+
+/* mu = ln tau - ln 2 */
+double orc_window_mu(float tau) { return log((double)tau) - log(2.0); }
+
+static int64_t orc_natural_index(const orc_geom *g, int p) {
+    return ((int64_t)g->fr[p] * g->H + g->hy[p]) * g->W + g->wx[p];
+}
+
+/* canonical window membership of the key at tile-major position j for the
+ * query at tile-major position i; lnT1 has N entries (ln t, t < N) */
+static int orc_is_member_1d(const orc_geom *g, const double *lnT1, double mu, float Hi, int i, int j) {
+    const int64_t a = orc_natural_index(g, i), b = orc_natural_index(g, j);
+    const int64_t d = a > b ? a - b : b - a;
+    if (d == 0) return 1;
+    return lnT1[d] <= (double)Hi + mu;
+}
+
+/* the same window written directly, fp64, no tables: 2 d <= tau * exp(H_i) */
+static int orc_is_member_1d_naive(const orc_geom *g, float Hi, float tau, int i, int j) {
+    const int64_t a = orc_natural_index(g, i), b = orc_natural_index(g, j);
+    const int64_t d = a > b ? a - b : b - a;
+    return 2.0 * (double)d <= orc_token_budget((double)Hi, (double)tau);
+}
+
+static double *orc_log_table_upto(int n) {
+    double *t = (double *)malloc(sizeof(double) * (size_t)(n > 1 ? n : 1));
+    if (t) orc_log_table(n - 1 > 0 ? n - 1 : 0, t);
+    return t;
+}
+
+/* Window support of one query (all N keys, tile-major positions). */
+int orc_member_row_1d(const float *ent, int F, int H, int W, float tau, int th, int tw, int i, uint8_t *member) {
+    orc_geom g = {0};
+    if (!ent || !member || orc_geom_init(&g, F, H, W, th, tw, tau, 0.0f)) { orc_geom_free(&g); return 1; }
+    if (i < 0 || i >= g.N) { orc_geom_free(&g); return 1; }
+    double *lnT1 = orc_log_table_upto(g.N);
+    if (!lnT1) { orc_geom_free(&g); return 1; }
+    const double mu = orc_window_mu(tau);
+    for (int j = 0; j < g.N; ++j) member[j] = (uint8_t)orc_is_member_1d(&g, lnT1, mu, ent[i], i, j);
+    free(lnT1);
+    orc_geom_free(&g);
+    return 0;
+}
+
+/* Pairs on which the canonical window test and the direct fp64 test disagree
+ * (all N*N pairs; tiny grids only). */
+int64_t orc_count_naive_disagreements_1d(const float *ent, int F, int H, int W, float tau, int th, int tw) {
+    orc_geom g = {0};
+    if (!ent || orc_geom_init(&g, F, H, W, th, tw, tau, 0.0f)) { orc_geom_free(&g); return -1; }
+    double *lnT1 = orc_log_table_upto(g.N);
+    if (!lnT1) { orc_geom_free(&g); return -1; }
+    const double mu = orc_window_mu(tau);
+    int64_t bad = 0;
+    for (int i = 0; i < g.N; ++i)
+        for (int j = 0; j < g.N; ++j)
+            bad += orc_is_member_1d(&g, lnT1, mu, ent[i], i, j) != orc_is_member_1d_naive(&g, ent[i], tau, i, j);
+    free(lnT1);
+    orc_geom_free(&g);
+    return bad;
+}
+
 /* Support of one query (all N keys, tile-major positions): member[j] in {0,1}.
  * ent: fp32 entropies in tile-major order. */
 int orc_member_row(const float *ent, int F, int H, int W, float tau, float gamma, int th, int tw,
@@ -355,7 +432,14 @@ typedef struct {
     const int32_t *qblocks;
     uint8_t *mask;
     int32_t *votes;
+    const double *lnT1; /* non-NULL: the 1D window support (orc_is_member_1d) instead of the disk */
+    double mu;
 } orc_mask_ctx;
+
+static int orc_mask_member(const orc_mask_ctx *c, int i, int j) {
+    if (c->lnT1) return orc_is_member_1d(c->g, c->lnT1, c->mu, c->ent[i], i, j);
+    return orc_is_member(c->g, c->ent[i], i, j);
+}
 
 static void orc_mask_body(void *vctx, int64_t lo, int64_t hi) {
     orc_mask_ctx *c = (orc_mask_ctx *)vctx;
@@ -371,7 +455,7 @@ static void orc_mask_body(void *vctx, int64_t lo, int64_t hi) {
         for (int i = q0; i < q1; ++i) {
             memset(touched, 0, (size_t)c->nkb);
             for (int j = 0; j < g->N; ++j)
-                if (orc_is_member(g, c->ent[i], i, j)) touched[j / c->bk] = 1;
+                if (orc_mask_member(c, i, j)) touched[j / c->bk] = 1;
             for (int kb = 0; kb < c->nkb; ++kb) vt[kb] += touched[kb];
         }
         for (int kb = 0; kb < c->nkb; ++kb) {
@@ -394,8 +478,31 @@ int orc_block_mask(const float *ent, int F, int H, int W, float tau, float gamma
     const int nqb = (g.N + bq - 1) / bq;
     for (int s = 0; s < nsel; ++s)
         if (qblocks[s] < 0 || qblocks[s] >= nqb) { orc_geom_free(&g); return 1; }
-    orc_mask_ctx c = {&g, ent, bq, bk, (g.N + bk - 1) / bk, vote_threshold, qblocks, mask, votes};
+    orc_mask_ctx c = {&g, ent, bq, bk, (g.N + bk - 1) / bk, vote_threshold, qblocks, mask, votes, NULL, 0.0};
     orc_parallel_for(nsel, nthreads, orc_mask_body, &c);
+    orc_geom_free(&g);
+    return 0;
+}
+
+/* The same block voting over the 1D window support (ablation variant): mask
+ * and votes of the selected q-blocks. */
+int orc_block_mask_1d(const float *ent, int F, int H, int W, float tau, int bq, int bk, int vote_threshold,
+                      int th, int tw, const int32_t *qblocks, int nsel, uint8_t *mask, int32_t *votes,
+                      int nthreads) {
+    orc_geom g = {0};
+    if (!ent || !qblocks || !mask || !votes || bq < 1 || bk < 1 || vote_threshold < 1 || nsel < 0)
+        return 1;
+    if (!(tau > 0.0f)) return 1;
+    if (orc_geom_init(&g, F, H, W, th, tw, tau, 0.0f)) { orc_geom_free(&g); return 1; }
+    const int nqb = (g.N + bq - 1) / bq;
+    for (int s = 0; s < nsel; ++s)
+        if (qblocks[s] < 0 || qblocks[s] >= nqb) { orc_geom_free(&g); return 1; }
+    double *lnT1 = orc_log_table_upto(g.N);
+    if (!lnT1) { orc_geom_free(&g); return 1; }
+    orc_mask_ctx c = {&g, ent, bq, bk, (g.N + bk - 1) / bk, vote_threshold, qblocks, mask, votes, lnT1,
+                      orc_window_mu(tau)};
+    orc_parallel_for(nsel, nthreads, orc_mask_body, &c);
+    free(lnT1);
     orc_geom_free(&g);
     return 0;
 }

@@ -25,6 +25,12 @@ int64_t orc_count_naive_disagreements(const float *ent, int F, int H, int W, flo
 int orc_block_mask(const float *ent, int F, int H, int W, float tau, float gamma, int bq, int bk,
                    int vote_threshold, int th, int tw, const int32_t *qblocks, int nsel, uint8_t *mask,
                    int32_t *votes, int nthreads);
+double orc_window_mu(float tau);
+int orc_member_row_1d(const float *ent, int F, int H, int W, float tau, int th, int tw, int i, uint8_t *member);
+int64_t orc_count_naive_disagreements_1d(const float *ent, int F, int H, int W, float tau, int th, int tw);
+int orc_block_mask_1d(const float *ent, int F, int H, int W, float tau, int bq, int bk, int vote_threshold,
+                      int th, int tw, const int32_t *qblocks, int nsel, uint8_t *mask, int32_t *votes,
+                      int nthreads);
 
 #define FAIL(msg)                                  \
     do {                                           \
@@ -100,9 +106,23 @@ int main(void) {
         for (int vote = 1; vote <= 3; ++vote)
             if (orc_block_mask(ent, F, H, W, 0.05f, 0.5f, bq, bk, vote, 8, 8, qb, nqb, mask, votes, 3))
                 FAIL("block_mask");
+        /* the 1D-window variant on the same entropies (NaN and infinities included) */
+        if (!(orc_window_mu(0.5f) < 0.0)) FAIL("window_mu");
+        if (orc_member_row_1d(ent, F, H, W, 0.05f, 4, 3, N - 1, member)) FAIL("member_row_1d");
+        if (orc_member_row_1d(ent, F, H, W, 0.05f, 8, 8, N, member) == 0) FAIL("member_row_1d accepted i = N");
+        if (orc_count_naive_disagreements_1d(ent + 5, 2, 6, 7, 0.1f, 4, 4) < 0) FAIL("naive disagreements 1d");
+        if (orc_count_naive_disagreements_1d(NULL, 2, 6, 7, 0.1f, 4, 4) >= 0) FAIL("1d disagreements accepted NULL");
+        for (int vote = 1; vote <= 3; ++vote)
+            if (orc_block_mask_1d(ent, F, H, W, 0.05f, bq, bk, vote, 8, 8, qb, nqb, mask, votes, 3))
+                FAIL("block_mask_1d");
+        if (orc_block_mask_1d(ent, F, H, W, 0.0f, bq, bk, 1, 8, 8, qb, nqb, mask, votes, 1) == 0)
+            FAIL("block_mask_1d accepted tau = 0");
+        if (orc_member_row_1d(ent, 1, 1, 1, 0.5f, 8, 8, 0, member)) FAIL("member_row_1d, N = 1");
         qb[0] = nqb;
         if (orc_block_mask(ent, F, H, W, 0.05f, 0.5f, bq, bk, 1, 8, 8, qb, 1, mask, votes, 1) == 0)
             FAIL("block_mask accepted a q-block past the end");
+        if (orc_block_mask_1d(ent, F, H, W, 0.05f, bq, bk, 1, 8, 8, qb, 1, mask, votes, 1) == 0)
+            FAIL("block_mask_1d accepted a q-block past the end");
         free(ent); free(member); free(mask); free(votes);
     }
     printf("oracle sanitize ok\n");
