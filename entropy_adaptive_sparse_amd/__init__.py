@@ -11,7 +11,7 @@ Functions (names as in the C ABI, without the ``tra_`` prefix):
     tile_major_permute / tile_major_unpermute
     dense_attn_entropy
     dense_attn_entropy_mask (the warm-up pass with the mask builder fused in)
-    build_block_mask, mask_prepare
+    build_block_mask, mask_prepare, natural_prepare
     block_sparse_attn
     dense_attn_entropy_natural, dense_attn_entropy_mask_natural, block_sparse_attn_natural
         (natural-order q, k, v, o; the tile-major map applied inside the kernels' loads and stores)
@@ -24,7 +24,7 @@ import threading
 
 __all__ = [
     "TraError", "library_path", "load", "tile_major_permute", "tile_major_unpermute", "dense_attn_entropy",
-    "dense_attn_entropy_mask", "build_block_mask", "mask_prepare", "block_sparse_attn",
+    "dense_attn_entropy_mask", "build_block_mask", "mask_prepare", "natural_prepare", "block_sparse_attn",
     "dense_attn_entropy_natural", "dense_attn_entropy_mask_natural", "block_sparse_attn_natural",
     "exported_symbols",
 ]
@@ -75,6 +75,7 @@ def load():
         lib.tra_build_block_mask.argtypes = [P, i32, i32, i32, i32, f32, f32, i32, i32, i32, i32, i32, P, P, i64,
                                              P, P]
         lib.tra_mask_prepare.argtypes = [i32, i32, i32, f32, f32, i32, i32, i32, i32]
+        lib.tra_natural_prepare.argtypes = [i32, i32, i32, i32, i32]
         lib.tra_block_sparse_attn.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, f32, i32, i32, P]
         lib.tra_dense_attn_entropy_mask.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f32, f32, f32,
                                                     i32, i32, i32, i32, i32, P, P, i64, P, P]
@@ -84,7 +85,7 @@ def load():
         lib.tra_block_sparse_attn_natural.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f32, i32,
                                                       i32, i32, i32, P]
         for name in ("tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
-                     "tra_build_block_mask", "tra_mask_prepare", "tra_block_sparse_attn",
+                     "tra_build_block_mask", "tra_mask_prepare", "tra_natural_prepare", "tra_block_sparse_attn",
                      "tra_dense_attn_entropy_mask", "tra_dense_attn_entropy_natural",
                      "tra_block_sparse_attn_natural", "tra_dense_attn_entropy_mask_natural"):
             getattr(lib, name).restype = i32
@@ -94,7 +95,8 @@ def load():
 
 def exported_symbols():
     return ["tra_status_string", "tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
-            "tra_build_block_mask", "tra_mask_prepare", "tra_block_sparse_attn", "tra_dense_attn_entropy_mask",
+            "tra_build_block_mask", "tra_mask_prepare", "tra_natural_prepare", "tra_block_sparse_attn",
+            "tra_dense_attn_entropy_mask",
             "tra_dense_attn_entropy_natural", "tra_block_sparse_attn_natural", "tra_dense_attn_entropy_mask_natural"]
 
 
@@ -123,6 +125,20 @@ def _dev(t, name):
     return t
 
 
+def _buf(t, name, shape, dtype, like):
+    """A caller-supplied buffer (input list or output), or a new one when t is None: on like's GPU,
+    contiguous, of exactly this shape and dtype, so that the kernels stay inside it."""
+    torch = _torch()
+    if t is None:
+        return torch.empty(tuple(shape), dtype=dtype, device=like.device)
+    _dev(t, name)
+    if t.device != like.device:
+        raise ValueError("%s is on %s, the inputs on %s" % (name, t.device, like.device))
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError("%s must be %s %s, got %s %s" % (name, dtype, tuple(shape), t.dtype, tuple(t.shape)))
+    return t
+
+
 def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
@@ -143,11 +159,11 @@ def _call(fn: str, *args) -> None:
 def tile_major_permute(x, F: int, H: int, W: int, tile_h: int = 8, tile_w: int = 8, out=None):
     """x [outer][N][row] (natural order) -> y in tile-major order.  Also accepts [outer][N]."""
     _dev(x, "x")
-    y = _torch().empty_like(x) if out is None else _dev(out, "out")
+    y = _buf(out, "out", x.shape, x.dtype, x)
     outer, N = x.shape[0], x.shape[1]
     row = 1 if x.dim() == 2 else int(x[0, 0].numel())
-    if N != F * H * W or y.shape != x.shape or y.dtype != x.dtype:
-        raise ValueError("shape mismatch")
+    if N != F * H * W:
+        raise ValueError("x has %d tokens, F*H*W = %d" % (N, F * H * W))
     _call("tra_tile_major_permute", _ptr(x), _ptr(y), outer, F, H, W, row, _dt(x), tile_h, tile_w, _stream(x))
     return y
 
@@ -155,11 +171,11 @@ def tile_major_permute(x, F: int, H: int, W: int, tile_h: int = 8, tile_w: int =
 def tile_major_unpermute(y, F: int, H: int, W: int, tile_h: int = 8, tile_w: int = 8, out=None):
     """y [outer][N][row] (tile-major) -> x in natural order."""
     _dev(y, "y")
-    x = _torch().empty_like(y) if out is None else _dev(out, "out")
+    x = _buf(out, "out", y.shape, y.dtype, y)
     outer, N = y.shape[0], y.shape[1]
     row = 1 if y.dim() == 2 else int(y[0, 0].numel())
-    if N != F * H * W or x.shape != y.shape or x.dtype != y.dtype:
-        raise ValueError("shape mismatch")
+    if N != F * H * W:
+        raise ValueError("y has %d tokens, F*H*W = %d" % (N, F * H * W))
     _call("tra_tile_major_unpermute", _ptr(y), _ptr(x), outer, F, H, W, row, _dt(y), tile_h, tile_w, _stream(y))
     return x
 
@@ -171,6 +187,8 @@ def _check_qkv(q, k, v):
             raise ValueError("%s must be [outer][N][D]" % n)
     if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share shape and dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
     return q.shape
 
 
@@ -179,13 +197,9 @@ def dense_attn_entropy(q, k, v, sm_scale: float | None = None, entropy: bool = T
     """Dense attention over all N keys with the per-query entropy (nats).  Returns (o, H, lse)."""
     torch = _torch()
     outer, N, D = _check_qkv(q, k, v)
-    o = torch.empty_like(q) if out is None else _dev(out, "out")
-    H = None
-    if entropy:
-        H = torch.empty((outer, N), dtype=torch.float32, device=q.device) if ent_out is None else ent_out
-    L = None
-    if lse:
-        L = torch.empty((outer, N), dtype=torch.float32, device=q.device) if lse_out is None else lse_out
+    o = _buf(out, "out", q.shape, q.dtype, q)
+    H = _buf(ent_out, "ent_out", (outer, N), torch.float32, q) if entropy else None
+    L = _buf(lse_out, "lse_out", (outer, N), torch.float32, q) if lse else None
     scale = (1.0 / D ** 0.5) if sm_scale is None else float(sm_scale)
     _call("tra_dense_attn_entropy", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(H), _ptr(L), outer, N, D, _dt(q),
           scale, _stream(q))
@@ -198,20 +212,14 @@ def _dense_mask(fn, q, k, v, F, H, W, tau, gamma, sm_scale, block_q, block_k, vo
     outer, N, D = _check_qkv(q, k, v)
     if N != F * H * W:
         raise ValueError("N must equal F*H*W")
-    dev = q.device
-    o = torch.empty_like(q) if out is None else _dev(out, "out")
-    Hh = None
-    if entropy:
-        Hh = torch.empty((outer, N), dtype=torch.float32, device=dev) if ent_out is None else ent_out
-    L = None
-    if lse:
-        L = torch.empty((outer, N), dtype=torch.float32, device=dev) if lse_out is None else lse_out
+    o = _buf(out, "out", q.shape, q.dtype, q)
+    Hh = _buf(ent_out, "ent_out", (outer, N), torch.float32, q) if entropy else None
+    L = _buf(lse_out, "lse_out", (outer, N), torch.float32, q) if lse else None
     nqb, nkb = -(-N // block_q), -(-N // block_k)
-    cnt = torch.empty((outer, nqb), dtype=torch.int32, device=dev) if kv_count is None else kv_count
-    idx = torch.empty((outer, nqb, nkb), dtype=torch.int32, device=dev) if kv_index is None else kv_index
-    msk = block_mask
-    if want_mask and msk is None:
-        msk = torch.empty((outer, nqb, nkb), dtype=torch.uint8, device=dev)
+    cnt = _buf(kv_count, "kv_count", (outer, nqb), torch.int32, q)
+    idx = _buf(kv_index, "kv_index", (outer, nqb, nkb), torch.int32, q)
+    msk = _buf(block_mask, "block_mask", (outer, nqb, nkb), torch.uint8, q) if (want_mask or block_mask is not None) \
+        else None
     scale = (1.0 / D ** 0.5) if sm_scale is None else float(sm_scale)
     _call(fn, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(Hh), _ptr(L), outer, F, H, W, D,
           _dt(q), scale, float(tau), float(gamma), block_q, block_k, int(vote_threshold), tile_h, tile_w, _ptr(cnt),
@@ -245,6 +253,11 @@ def mask_prepare(F, H, W, tau, gamma, block_q=128, block_k=64, tile_h=8, tile_w=
     _call("tra_mask_prepare", F, H, W, float(tau), float(gamma), block_q, block_k, tile_h, tile_w)
 
 
+def natural_prepare(F, H, W, tile_h=8, tile_w=8) -> None:
+    """Build and upload the tile-major map of the natural-order calls ahead of a timed region."""
+    _call("tra_natural_prepare", F, H, W, tile_h, tile_w)
+
+
 def build_block_mask(entropy, F: int, H: int, W: int, tau: float, gamma: float, block_q: int = 128,
                      block_k: int = 64, vote_threshold: int = 1, tile_h: int = 8, tile_w: int = 8,
                      want_mask: bool = False, kv_count=None, kv_index=None, block_mask=None):
@@ -255,12 +268,10 @@ def build_block_mask(entropy, F: int, H: int, W: int, tau: float, gamma: float, 
         raise ValueError("entropy must be float32 [outer][N]")
     outer, N = entropy.shape
     nqb, nkb = -(-N // block_q), -(-N // block_k)
-    dev = entropy.device
-    cnt = torch.empty((outer, nqb), dtype=torch.int32, device=dev) if kv_count is None else kv_count
-    idx = torch.empty((outer, nqb, nkb), dtype=torch.int32, device=dev) if kv_index is None else kv_index
-    msk = block_mask
-    if want_mask and msk is None:
-        msk = torch.empty((outer, nqb, nkb), dtype=torch.uint8, device=dev)
+    cnt = _buf(kv_count, "kv_count", (outer, nqb), torch.int32, entropy)
+    idx = _buf(kv_index, "kv_index", (outer, nqb, nkb), torch.int32, entropy)
+    msk = _buf(block_mask, "block_mask", (outer, nqb, nkb), torch.uint8, entropy) \
+        if (want_mask or block_mask is not None) else None
     _call("tra_build_block_mask", _ptr(entropy), outer, F, H, W, float(tau), float(gamma), block_q, block_k,
           int(vote_threshold), tile_h, tile_w, _ptr(cnt), _ptr(idx), idx.numel(), _ptr(msk), _stream(entropy))
     return cnt, idx, msk
@@ -271,17 +282,13 @@ def block_sparse_attn(q, k, v, kv_count, kv_index, block_q: int = 128, block_k: 
     """Attention of each query over the tokens of its q-block's retained k-blocks.  Returns (o, lse)."""
     torch = _torch()
     outer, N, D = _check_qkv(q, k, v)
-    _dev(kv_count, "kv_count")
-    _dev(kv_index, "kv_index")
     nqb, nkb = -(-N // block_q), -(-N // block_k)
-    if tuple(kv_count.shape) != (outer, nqb) or tuple(kv_index.shape) != (outer, nqb, nkb):
-        raise ValueError("kv_count/kv_index shape does not match N, block_q, block_k")
-    if kv_count.dtype != torch.int32 or kv_index.dtype != torch.int32:
-        raise ValueError("kv_count/kv_index must be int32")
-    o = torch.empty_like(q) if out is None else _dev(out, "out")
-    L = None
-    if lse:
-        L = torch.empty((outer, N), dtype=torch.float32, device=q.device) if lse_out is None else lse_out
+    if kv_count is None or kv_index is None:
+        raise ValueError("kv_count and kv_index are required")
+    _buf(kv_count, "kv_count", (outer, nqb), torch.int32, q)
+    _buf(kv_index, "kv_index", (outer, nqb, nkb), torch.int32, q)
+    o = _buf(out, "out", q.shape, q.dtype, q)
+    L = _buf(lse_out, "lse_out", (outer, N), torch.float32, q) if lse else None
     scale = (1.0 / D ** 0.5) if sm_scale is None else float(sm_scale)
     _call("tra_block_sparse_attn", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), _ptr(kv_count), _ptr(kv_index),
           outer, N, D, _dt(q), scale, block_q, block_k, _stream(q))
@@ -297,13 +304,9 @@ def dense_attn_entropy_natural(q, k, v, F: int, H: int, W: int, sm_scale: float 
     outer, N, D = _check_qkv(q, k, v)
     if N != F * H * W:
         raise ValueError("N must equal F*H*W")
-    o = torch.empty_like(q) if out is None else _dev(out, "out")
-    Hh = None
-    if entropy:
-        Hh = torch.empty((outer, N), dtype=torch.float32, device=q.device) if ent_out is None else ent_out
-    L = None
-    if lse:
-        L = torch.empty((outer, N), dtype=torch.float32, device=q.device) if lse_out is None else lse_out
+    o = _buf(out, "out", q.shape, q.dtype, q)
+    Hh = _buf(ent_out, "ent_out", (outer, N), torch.float32, q) if entropy else None
+    L = _buf(lse_out, "lse_out", (outer, N), torch.float32, q) if lse else None
     scale = (1.0 / D ** 0.5) if sm_scale is None else float(sm_scale)
     _call("tra_dense_attn_entropy_natural", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(Hh), _ptr(L), outer, F, H, W,
           D, _dt(q), scale, tile_h, tile_w, _stream(q))
@@ -319,17 +322,13 @@ def block_sparse_attn_natural(q, k, v, kv_count, kv_index, F: int, H: int, W: in
     outer, N, D = _check_qkv(q, k, v)
     if N != F * H * W:
         raise ValueError("N must equal F*H*W")
-    _dev(kv_count, "kv_count")
-    _dev(kv_index, "kv_index")
     nqb, nkb = -(-N // block_q), -(-N // block_k)
-    if tuple(kv_count.shape) != (outer, nqb) or tuple(kv_index.shape) != (outer, nqb, nkb):
-        raise ValueError("kv_count/kv_index shape does not match N, block_q, block_k")
-    if kv_count.dtype != torch.int32 or kv_index.dtype != torch.int32:
-        raise ValueError("kv_count/kv_index must be int32")
-    o = torch.empty_like(q) if out is None else _dev(out, "out")
-    L = None
-    if lse:
-        L = torch.empty((outer, N), dtype=torch.float32, device=q.device) if lse_out is None else lse_out
+    if kv_count is None or kv_index is None:
+        raise ValueError("kv_count and kv_index are required")
+    _buf(kv_count, "kv_count", (outer, nqb), torch.int32, q)
+    _buf(kv_index, "kv_index", (outer, nqb, nkb), torch.int32, q)
+    o = _buf(out, "out", q.shape, q.dtype, q)
+    L = _buf(lse_out, "lse_out", (outer, N), torch.float32, q) if lse else None
     scale = (1.0 / D ** 0.5) if sm_scale is None else float(sm_scale)
     _call("tra_block_sparse_attn_natural", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), _ptr(kv_count),
           _ptr(kv_index), outer, F, H, W, D, _dt(q), scale, block_q, block_k, tile_h, tile_w, _stream(q))

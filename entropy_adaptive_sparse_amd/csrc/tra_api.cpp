@@ -472,6 +472,14 @@ tra_status tra_dense_attn_entropy_mask_natural(const void *q, const void *k, con
                            true);
 }
 
+tra_status tra_natural_prepare(int F, int H, int W, int tile_h, int tile_w) {
+    TileGeom g;
+    const tra_status st = check_natural(F, H, W, 128, TRA_BF16, tile_h, tile_w, g);
+    if (st != TRA_OK) return st;
+    const int32_t *map = nullptr;
+    return get_nat_table(g, map);
+}
+
 tra_status tra_dense_attn_entropy_natural(const void *q, const void *k, const void *v, void *o, float *entropy,
                                           float *lse, int outer, int F, int H, int W, int D, tra_dtype dt,
                                           float sm_scale, int tile_h, int tile_w, hipStream_t s) {

@@ -28,9 +28,9 @@
  *  - Library state: a per-device cache of small fp64 tables and block
  *    geometry for tra_build_block_mask, and of the tile-major map for the
  *    natural-order attention calls, guarded by a mutex.  Its first use for a
- *    geometry allocates and uploads them synchronously (tra_mask_prepare
- *    does that ahead of time for the mask); entries live until the process
- *    ends.
+ *    geometry allocates and uploads them synchronously (tra_mask_prepare and
+ *    tra_natural_prepare do that ahead of time); entries live until the
+ *    process ends.
  */
 #ifndef TRA_H_
 #define TRA_H_
@@ -206,8 +206,9 @@ tra_status tra_dense_attn_entropy_mask(const void *q, const void *k, const void 
  * group of four tile-major positions is a run of four natural rows), N*D*2 <
  * 2^32; sparse: block_q = 128, block_k = 64.  Anything else returns
  * TRA_ERR_UNSUPPORTED before any HIP call.  The first call for a geometry
- * builds and uploads the map (N/4 int32 natural row indices) synchronously;
- * it stays in the per-device cache until the process ends.
+ * builds and uploads the map (N/4 int32 natural row indices) synchronously
+ * (tra_natural_prepare does that ahead of time); it stays in the per-device
+ * cache until the process ends.
  */
 /*
  * tra_dense_attn_entropy_mask on natural-order q, k, v, o (the warm-up step in one call):
@@ -221,6 +222,11 @@ tra_status tra_dense_attn_entropy_mask_natural(const void *q, const void *k, con
                                                int vote_threshold, int tile_h, int tile_w, int32_t *kv_count,
                                                int32_t *kv_index, int64_t kv_index_capacity, uint8_t *block_mask,
                                                hipStream_t s);
+/* Builds and uploads the tile-major map the natural-order calls use for this geometry on the
+ * current device (blocking), so that a timed call does no allocation or upload.  Returns
+ * TRA_ERR_UNSUPPORTED for the geometries those calls reject (W or tile_w not a multiple of 4),
+ * TRA_ERR_INVALID_ARG for non-positive sizes. */
+tra_status tra_natural_prepare(int F, int H, int W, int tile_h, int tile_w);
 tra_status tra_dense_attn_entropy_natural(const void *q, const void *k, const void *v, void *o, float *entropy,
                                           float *lse, int outer, int F, int H, int W, int D, tra_dtype dt,
                                           float sm_scale, int tile_h, int tile_w, hipStream_t s);

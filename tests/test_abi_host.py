@@ -37,7 +37,7 @@ def test_header_declares_the_entry_points():
     for n in ("tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
               "tra_build_block_mask", "tra_block_sparse_attn", "tra_mask_prepare", "tra_status_string",
               "tra_dense_attn_entropy_mask", "tra_dense_attn_entropy_natural", "tra_block_sparse_attn_natural",
-              "tra_dense_attn_entropy_mask_natural"):
+              "tra_dense_attn_entropy_mask_natural", "tra_natural_prepare"):
         assert n in names
 
 
@@ -197,6 +197,14 @@ def test_natural_order_validation(lib):
     assert call(ff, fused, a11=F32) == UNSUPPORTED                # fp32
     assert call(ff, fused, a7=65, a8=8, a9=8) == UNSUPPORTED      # more frames than the tile buffers hold
     assert call(ff, fused, a22=2 * 8 * 16 - 1) == CAPACITY        # kv_index capacity
+
+
+def test_natural_prepare_validation(lib):
+    f = lib.tra_natural_prepare
+    assert f(0, 16, 16, 8, 8) == INVALID            # F
+    assert f(4, 16, 16, 0, 8) == INVALID            # tile height
+    assert f(4, 16, 18, 8, 8) == UNSUPPORTED        # W not a multiple of 4
+    assert f(4, 16, 16, 8, 6) == UNSUPPORTED        # tile width not a multiple of 4
 
 
 def test_header_is_plain_c(tmp_path):
