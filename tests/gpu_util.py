@@ -70,3 +70,92 @@ def sample_rows(seed, N, bq, nblocks):
     blocks = synth.uniform_ints(seed, nblocks - 1, 0, nqb - 1).tolist() + [nqb - 1]  # always the ragged one
     rows = np.concatenate([np.arange(b * bq, min(N, b * bq + bq)) for b in blocks]).astype(np.int32)
     return np.array(blocks, dtype=np.int32), rows
+
+
+# ------------------------------------------------------------------------------------------------
+# oracle references for the calls whose mask comes from their own entropies
+# ------------------------------------------------------------------------------------------------
+ENT_TOL = 1e-3
+LSE_TOL = 1e-3
+
+
+def np64(x):
+    return x.float().numpy().astype(np.float64)
+
+
+def fp32_below(x64):
+    """the largest fp32 values <= x64 (elementwise)"""
+    f = np.asarray(x64, dtype=np.float64).astype(np.float32)
+    return np.where(f.astype(np.float64) > x64, np.nextafter(f, np.float32(-np.inf)), f)
+
+
+def fp32_above(x64):
+    """the smallest fp32 values >= x64 (elementwise)"""
+    f = np.asarray(x64, dtype=np.float64).astype(np.float32)
+    return np.where(f.astype(np.float64) < x64, np.nextafter(f, np.float32(np.inf)), f)
+
+
+def mask_bounds(orc, wl, ent64, rows, blocks, vote, delta=ENT_TOL):
+    """Oracle mask rows of the q-blocks `blocks` (tile-major) built from the oracle's own fp64
+    entropies of their queries (ent64[r] for tile-major position rows[r]) moved down and up by
+    delta, rounded outward to fp32.  A query's disk grows with its entropy in every frame, so vote
+    counts and retention are monotone in the entropies: any fp32 entropies within delta of the
+    oracle's give a mask between the two returned masks (lo <= mask <= hi).  Where lo == hi the
+    mask is fixed exactly; elsewhere both values are within the entropy tolerance."""
+    lo_e = np.zeros(wl.N, dtype=np.float32)
+    hi_e = np.zeros(wl.N, dtype=np.float32)
+    lo_e[rows] = fp32_below(ent64 - delta)
+    hi_e[rows] = fp32_above(ent64 + delta)
+    kw = dict(qblocks=np.asarray(blocks, dtype=np.int32))
+    lo, _ = orc.block_mask(lo_e, wl.F, wl.H, wl.W, wl.tau, wl.gamma, wl.block_q, wl.block_k, vote, wl.tile_h,
+                           wl.tile_w, **kw)
+    hi, _ = orc.block_mask(hi_e, wl.F, wl.H, wl.W, wl.tau, wl.gamma, wl.block_q, wl.block_k, vote, wl.tile_h,
+                           wl.tile_w, **kw)
+    assert np.all(lo <= hi), "oracle mask not monotone in the entropy"
+    return lo, hi
+
+
+def check_mask_rows(msk, cnt, idx, lo, hi, what):
+    """GPU mask rows (msk [S][nkb], cnt [S], idx [S][nkb]) against the oracle's bounds; the lists
+    must be the ascending retained k-blocks of the mask.  Returns the number of entries the bounds
+    leave open (decided by entropy differences within the tolerance)."""
+    assert np.all(msk >= lo) and np.all(msk <= hi), "%s: mask outside the oracle's bounds" % what
+    for s in range(msk.shape[0]):
+        nz = np.nonzero(msk[s])[0]
+        assert cnt[s] == len(nz), "%s: row %d kv_count" % (what, s)
+        assert np.array_equal(idx[s, :cnt[s]], nz), "%s: row %d kv_index" % (what, s)
+    return int((lo != hi).sum())
+
+
+def rows_of_blocks(blocks, N, bq):
+    return np.concatenate([np.arange(b * bq, min(N, b * bq + bq)) for b in blocks]).astype(np.int32)
+
+
+def check_warmup_against_oracle(orc, wl, qkv_cpu, out, heads, blocks, vote, natural):
+    """out = (o, entropy, lse, kv_count, kv_index, block_mask) of a fused warm-up call (GPU tensors;
+    o in natural order when `natural`, everything else by tile-major position); qkv_cpu: the
+    natural-order inputs.  Checks the q-blocks `blocks` of the heads `heads` against the oracle."""
+    torch = torch_mod()
+    o, Hh, L, cnt, idx, msk = out
+    qc, kc, vc = qkv_cpu
+    perm = orc.tile_major_order(wl.F, wl.H, wl.W, wl.tile_h, wl.tile_w)
+    rows = rows_of_blocks(blocks, wl.N, wl.block_q)
+    nat = perm[rows].astype(np.int64)
+    open_entries = 0
+    worst = [0.0, 0.0, 0.0]
+    for h in heads:
+        ro, rH, rL = orc.attention(np64(qc[h]), np64(kc[h]), np64(vc[h]), wl.sm_scale, rows=nat.astype(np.int32))
+        sel = torch.from_numpy(nat if natural else rows.astype(np.int64)).to(o.device)
+        err, _ = check_output(o[h].index_select(0, sel).float().cpu().numpy(), ro, "bf16")
+        r = torch.from_numpy(rows.astype(np.int64)).to(o.device)
+        e_ent = float(np.max(np.abs(Hh[h].index_select(0, r).cpu().numpy() - rH)))
+        e_lse = float(np.max(np.abs(L[h].index_select(0, r).cpu().numpy() - rL)))
+        assert e_ent <= ENT_TOL, "head %d entropy err %.3g" % (h, e_ent)
+        assert e_lse <= LSE_TOL, "head %d lse err %.3g" % (h, e_lse)
+        lo, hi = mask_bounds(orc, wl, rH, rows, blocks, vote)
+        b = torch.from_numpy(np.asarray(blocks, dtype=np.int64)).to(o.device)
+        open_entries += check_mask_rows(msk[h].index_select(0, b).cpu().numpy(), cnt[h].index_select(0, b).cpu().numpy(),
+                                        idx[h].index_select(0, b).cpu().numpy(), lo, hi, "head %d" % h)
+        worst = [max(worst[0], err), max(worst[1], e_ent), max(worst[2], e_lse)]
+    say("  vs oracle: max-abs out %.3g, entropy %.3g, lse %.3g; mask entries left open by the entropy "
+        "tolerance: %d of %d" % (*worst, open_entries, len(heads) * len(blocks) * wl.nkb))

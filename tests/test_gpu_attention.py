@@ -327,3 +327,69 @@ def test_rising_scores_force_max_moves(orc, dtype, slope):
     od, _, Ld = t.dense_attn_entropy(qp, kp, vp, wl.sm_scale, entropy=False, lse=True)
     torch.cuda.synchronize()
     assert torch.equal(os_, od) and torch.equal(Ls, Ld)  # every block retained: the dense result, bit for bit
+
+
+@pytest.mark.parametrize("dtype,natural", [("bf16", False), ("f32", False), ("bf16", True)])
+def test_sparse_invalid_lists_stay_inside(orc, dtype, natural):
+    # Lists that break the contract -- the ragged last k-block at positions 0-2 (and again later),
+    # duplicates, negative and too-large entries, a count above nkb -- are clamped as the header
+    # states: every access stays inside k and v.  k and v end where a buffer holding NaN rows
+    # begins, so a row read past N that entered a softmax would turn the output into NaN.  The
+    # q-blocks with valid lists in the same call still match the oracle.
+    torch = torch_mod()
+    t = tra()
+    dev = device()
+    F, H, W, D = 1, 25, 40, 128   # N = 1000: nkb = 16 with a ragged 40-row k-block, nqb = 8
+    wl = small_workload(170, F, H, W, D, dtype)
+    N, nkb, nqb, outer = wl.N, wl.nkb, wl.nqb, wl.outer
+    say("sparse invalid lists", dtype, "natural" if natural else "tile-major")
+    q, k, v = qkv_inputs(wl)
+    tdt = q.dtype
+    bufs = []
+    for x in (k, v):
+        big = torch.full((outer * N + 256, D), float("nan"), dtype=tdt, device=dev)
+        big[:outer * N] = x.reshape(outer * N, D).to(dev)
+        bufs.append(big)
+    kd, vd = (b[:outer * N].view(outer, N, D) for b in bufs)
+    qd = q.to(dev)
+    rng = np.random.default_rng(171)
+    cnt = np.zeros((outer, nqb), dtype=np.int32)
+    idx = np.zeros((outer, nqb, nkb), dtype=np.int32)
+    mask = np.zeros((outer, nqb, nkb), dtype=np.uint8)
+    for h in range(outer):
+        for qb in range(nqb):
+            if qb < 4:  # invalid lists
+                n = nkb
+                row = rng.integers(0, nkb, size=n).astype(np.int32)
+                row[qb % 3] = nkb - 1
+                row[(qb + 5) % n] = nkb - 1
+                row[7] = -3 - qb
+                row[9] = nkb + 40 * qb
+                cnt[h, qb] = n + 3 * qb  # above nkb for qb > 0: clamped to nkb
+                idx[h, qb] = row
+            else:       # valid lists, the ragged k-block last in half of them
+                n = 5 + qb
+                chosen = np.sort(rng.choice(nkb - 1, size=n - (qb % 2), replace=False))
+                if qb % 2:
+                    chosen = np.append(chosen, nkb - 1)
+                cnt[h, qb] = len(chosen)
+                idx[h, qb, :len(chosen)] = chosen
+                mask[h, qb, chosen] = 1
+    cd, id_ = torch.from_numpy(cnt).to(dev), torch.from_numpy(idx).to(dev)
+    if natural:
+        qn, kn, vn = qd, kd, vd
+        o_nat, L = t.block_sparse_attn_natural(qn, kn, vn, cd, id_, F, H, W, wl.block_q, wl.block_k, wl.sm_scale,
+                                               lse=True)
+        o = t.tile_major_permute(o_nat, F, H, W)
+    else:
+        # tile-major copies whose k and v again end where the NaN rows begin
+        for b, x in zip(bufs, (kd, vd)):
+            b[:outer * N] = t.tile_major_permute(x.clone(), F, H, W).reshape(outer * N, D)
+        qp = t.tile_major_permute(qd, F, H, W)
+        o, L = t.block_sparse_attn(qp, kd, vd, cd, id_, wl.block_q, wl.block_k, wl.sm_scale, lse=True)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    L = L.cpu().numpy()
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(L)), "a row past N reached the softmax"
+    rows = np.arange(4 * wl.block_q, N, dtype=np.int32)
+    _check_sparse(orc, wl, q, k, v, o, L, mask, range(outer), rows)

@@ -1,29 +1,34 @@
 """GPU: the fused warm-up pass (dense attention + entropy with the mask builder as its
 epilogue, two q-blocks' rows per workgroup; "Token Radius Attention for Efficient Video
-Generation", section 2, TRA pipeline steps 1-3) equals the two separate calls bit for bit.
+Generation", section 2, TRA pipeline steps 1-3).
 
-The separate calls are pinned to the oracle elsewhere: tra_dense_attn_entropy in
-test_gpu_attention.py (outputs, entropy and lse within tolerance), tra_build_block_mask in
-test_gpu_mask.py (bit-exact masks from entropies the oracle also sees).  Here the fused
-mask is compared with tra_build_block_mask applied to the fused call's own entropies, and
-its o, entropy and lse with tra_dense_attn_entropy's: no oracle value comes from the GPU.
+Two checks:
+- against the oracle: o, entropy and lse within the attention tolerances of the oracle's
+  fp64 attention on the same bf16 inputs; the mask rows between the oracle's masks built
+  from its own entropies moved down and up by the entropy tolerance (exact wherever the two
+  agree; gpu_util.mask_bounds), and kv_count / kv_index the ascending lists of those rows.
+  No oracle input comes from the GPU.
+- bit for bit against the two separate calls (tra_dense_attn_entropy, then
+  tra_build_block_mask on the fused call's own entropies).
 """
 import numpy as np
 import pytest
 
 from entropy_adaptive_sparse_amd import workloads
-from gpu_util import device, qkv_inputs, say, small_workload, torch_mod, tra
+from entropy_adaptive_sparse_amd import synth
+from gpu_util import (check_warmup_against_oracle, device, qkv_inputs, sample_rows, say, small_workload, torch_mod,
+                      tra)
 
 pytestmark = pytest.mark.gpu
 
 
-def _tile_major(t, wl):
-    torch = torch_mod()
-    q, k, v = qkv_inputs(wl)
+def _tile_major(t, wl, qkv=None):
+    q, k, v = qkv_inputs(wl) if qkv is None else qkv
     return tuple(t.tile_major_permute(x.to(device()), wl.F, wl.H, wl.W) for x in (q, k, v))
 
 
 def _compare(t, wl, q, k, v, vote):
+    """fused call vs the separate calls, bit for bit; returns the fused call's outputs"""
     torch = torch_mod()
     o1, h1, l1, c1, i1, m1 = t.dense_attn_entropy_mask(q, k, v, wl.F, wl.H, wl.W, wl.tau, wl.gamma, wl.sm_scale,
                                                        wl.block_q, wl.block_k, vote, entropy=True, lse=True,
@@ -42,7 +47,9 @@ def _compare(t, wl, q, k, v, vote):
     for h in range(c.shape[0]):
         for qb in range(c.shape[1]):
             assert np.array_equal(a[h, qb, :c[h, qb]], b[h, qb, :c[h, qb]]), (h, qb)
-    return float(m1.float().mean().item())
+    del o2, h2, l2, c2, i2, m2
+    say("  block density", float(m1.float().mean().item()))
+    return o1, h1, l1, c1, i1, m1
 
 
 @pytest.mark.parametrize("F,H,W,tau,gamma,vote", [
@@ -56,24 +63,33 @@ def _compare(t, wl, q, k, v, vote):
     (2, 8, 8, 0.05, 0.5, 2),         # exactly one q-block
     (3, 7, 9, 0.05, 0.5, 1),         # N = 189: two q-blocks, the second ragged
 ])
-def test_fused_equals_separate(F, H, W, tau, gamma, vote):
+def test_fused_small_full(orc, F, H, W, tau, gamma, vote):
+    # every query and every q-block of both heads against the oracle, and bit for bit against
+    # the separate calls
     t = tra()
     wl = small_workload(200 + F + H + W, F, H, W, 128, "bf16", tau=tau, gamma=gamma, vote=vote)
     say("fused warm-up", F, H, W, tau, gamma, vote)
-    q, k, v = _tile_major(t, wl)
-    dens = _compare(t, wl, q, k, v, vote)
-    say("  block density", dens)
+    qkv = qkv_inputs(wl)
+    q, k, v = _tile_major(t, wl, qkv)
+    out = _compare(t, wl, q, k, v, vote)
+    check_warmup_against_oracle(orc, wl, qkv, out, range(wl.outer), np.arange(wl.nqb), vote, natural=False)
 
 
 @pytest.mark.parametrize("wid", [3, 4])  # 4: 33 frames, thresholds in both split buffers
-def test_fused_full_size(wid):
+def test_fused_full_size(orc, wid):
+    # every head and q-block on the GPU; seeded q-blocks (the ragged last one included) of two
+    # seeded heads against the oracle
     t = tra()
     wl = workloads.get(wid)
     say("fused warm-up at full size", wl.name)
-    q, k, v = _tile_major(t, wl)
+    qkv = qkv_inputs(wl)
+    q, k, v = _tile_major(t, wl, qkv)
     t.mask_prepare(wl.F, wl.H, wl.W, wl.tau, wl.gamma, wl.block_q, wl.block_k)
-    dens = _compare(t, wl, q, k, v, wl.vote_threshold)
-    say("  block density", dens)
+    out = _compare(t, wl, q, k, v, wl.vote_threshold)
+    del q, k, v
+    blocks, _ = sample_rows(40 + wid, wl.N, wl.block_q, 3)
+    heads = synth.uniform_ints(50 + wid, 2, 0, wl.outer)
+    check_warmup_against_oracle(orc, wl, qkv, out, heads, blocks, wl.vote_threshold, natural=False)
 
 
 def test_fused_rejects_unsupported():

@@ -57,6 +57,24 @@ def test_mask_small_all_blocks(orc, F, H, W, tau, gamma, bq, vote):
     _compare(orc, ent, cnt, idx, msk, F, H, W, tau, gamma, bq, 64, vote, heads=range(2))
 
 
+@pytest.mark.parametrize("tile", [(1, 1), (3, 5), (4, 16), (16, 16), (2, 8)])
+@pytest.mark.parametrize("F,H,W,tau,gamma,bq,vote", [
+    (4, 16, 16, 0.03, 0.5, 128, 1),
+    (3, 15, 17, 0.02, 0.3, 64, 2),     # clipped tiles on both edges
+    (6, 9, 22, 0.1, 0.5, 128, 1),
+])
+def test_mask_tile_shapes(orc, tile, F, H, W, tau, gamma, bq, vote):
+    # the k-block rectangles, the reach windows (rounded out to whole tiles) and the tile-major
+    # ranges all depend on the tile shape: every q-block of both heads, bit for bit
+    t = tra()
+    N = F * H * W
+    th, tw = tile
+    say("mask tile shape", tile, F, H, W, tau, gamma, bq, vote)
+    ent = synth.entropy_like(F * 11 + W + th, 2, N)
+    cnt, idx, msk = _gpu_mask(t, ent, F, H, W, tau, gamma, bq, 64, vote, th, tw)
+    _compare(orc, ent, cnt, idx, msk, F, H, W, tau, gamma, bq, 64, vote, heads=range(2), th=th, tw=tw)
+
+
 @pytest.mark.parametrize("bq,vote", [(128, 1), (64, 1), (128, 3)])
 def test_mask_special_entropies(orc, bq, vote):
     # NaN and -inf reach only distance 0, +inf the whole frame; negative, zero and

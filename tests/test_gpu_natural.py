@@ -1,19 +1,22 @@
 """GPU: the natural-order attention calls (the tile-major permutation of "Token Radius
 Attention for Efficient Video Generation", section 2, TRA pipeline step 3, applied inside
-the kernels' loads and stores) equal the permute -> tile-major call -> unpermute chain bit
-for bit, and the oracle within the attention tolerances.
+the kernels' loads and stores).
 
-The tile-major calls are pinned to the oracle in test_gpu_attention.py; here the natural
-calls are compared with them on the same inputs (o in natural order, entropy and lse by
-tile-major position), plus one direct oracle check in natural order.
+Each call is compared
+- with the oracle directly: outputs in natural order within the attention tolerances of the
+  oracle's fp64 attention (dense, or restricted to the oracle's block mask), entropy and lse
+  by tile-major position; the fused warm-up's mask rows between the oracle's bounds
+  (gpu_util.mask_bounds) -- on small grids in full and on seeded q-blocks at full size;
+- with the permute -> tile-major call -> unpermute chain, bit for bit.
 """
 import dataclasses
 
 import numpy as np
 import pytest
 
-from entropy_adaptive_sparse_amd import workloads
-from gpu_util import check_output, device, qkv_inputs, say, small_workload, torch_mod, tra
+from entropy_adaptive_sparse_amd import synth, workloads
+from gpu_util import (LSE_TOL, check_output, check_warmup_against_oracle, device, np64, qkv_inputs, rows_of_blocks,
+                      sample_rows, say, small_workload, torch_mod, tra)
 
 pytestmark = pytest.mark.gpu
 
@@ -116,12 +119,13 @@ def test_natural_sparse_every_list_length():
     (3, 21, 24, (6, 12), 1),
     (1, 4, 8, (8, 8), 1),     # one ragged q-block
 ])
-def test_natural_fused_warmup_equals_tile_major(F, H, W, tile, vote):
+def test_natural_fused_warmup(orc, F, H, W, tile, vote):
     torch = torch_mod()
     t = tra()
     wl = _wl(400 + F + H + W, F, H, W, tile)
     say("natural fused warm-up", F, H, W, tile, vote)
-    q, k, v = (x.to(device()) for x in qkv_inputs(wl))
+    qkv = qkv_inputs(wl)
+    q, k, v = (x.to(device()) for x in qkv)
     th, tw = tile
     qp, kp, vp = (t.tile_major_permute(x, F, H, W, th, tw) for x in (q, k, v))
     args = (F, H, W, wl.tau, wl.gamma, wl.sm_scale, wl.block_q, wl.block_k, vote, th, tw)
@@ -136,6 +140,114 @@ def test_natural_fused_warmup_equals_tile_major(F, H, W, tile, vote):
     for hh in range(c.shape[0]):
         for qb in range(c.shape[1]):
             assert np.array_equal(a[hh, qb, :c[hh, qb]], b[hh, qb, :c[hh, qb]]), (hh, qb)
+    # every query and q-block of both heads against the oracle
+    check_warmup_against_oracle(orc, wl, qkv, (o2, h2, l2, c2, i2, m2), range(wl.outer), np.arange(wl.nqb), vote,
+                                natural=True)
+
+
+@pytest.mark.parametrize("wid", [3, 4])
+def test_natural_fused_full_size(orc, wid):
+    # natural-order fused warm-up over every head and q-block; seeded q-blocks (the ragged last one
+    # included) of two seeded heads against the oracle
+    t = tra()
+    wl = workloads.get(wid)
+    say("natural fused warm-up at full size", wl.name)
+    qkv = qkv_inputs(wl)
+    q, k, v = (x.to(device()) for x in qkv)
+    t.mask_prepare(wl.F, wl.H, wl.W, wl.tau, wl.gamma, wl.block_q, wl.block_k)
+    t.natural_prepare(wl.F, wl.H, wl.W)
+    out = t.dense_attn_entropy_mask_natural(q, k, v, wl.F, wl.H, wl.W, wl.tau, wl.gamma, wl.sm_scale, wl.block_q,
+                                            wl.block_k, wl.vote_threshold, lse=True, want_mask=True)
+    torch_mod().cuda.synchronize()
+    del q, k, v
+    blocks, _ = sample_rows(60 + wid, wl.N, wl.block_q, 3)
+    heads = synth.uniform_ints(70 + wid, 2, 0, wl.outer)
+    check_warmup_against_oracle(orc, wl, qkv, out, heads, blocks, wl.vote_threshold, natural=True)
+
+
+def _lists_from_mask(mask):
+    """mask [outer][nqb][nkb] -> int32 kv_count, kv_index (ascending, padded with -3)"""
+    outer, nqb, nkb = mask.shape
+    cnt = mask.sum(axis=2).astype(np.int32)
+    idx = np.full((outer, nqb, nkb), -3, dtype=np.int32)
+    for o in range(outer):
+        for qb in range(nqb):
+            nz = np.nonzero(mask[o, qb])[0]
+            idx[o, qb, :len(nz)] = nz
+    return cnt, idx
+
+
+def _check_sparse_natural(orc, wl, qkv, o_nat, L, mask, heads, blocks):
+    """natural-order sparse output rows of the q-blocks `blocks` vs the oracle's masked attention
+    (tile-major positions, mask [nqb][nkb] per head), mapped to natural order"""
+    torch = torch_mod()
+    perm = orc.tile_major_order(wl.F, wl.H, wl.W, wl.tile_h, wl.tile_w)
+    rows = rows_of_blocks(blocks, wl.N, wl.block_q)
+    worst = 0.0
+    for h in heads:
+        qp, kp, vp = (orc.permute(np64(x[h]), perm) for x in qkv)
+        ro, _, rL = orc.attention(qp, kp, vp, wl.sm_scale, rows=rows, block_mask=mask[h], bq=wl.block_q,
+                                  bk=wl.block_k)
+        sel = torch.from_numpy(perm[rows].astype(np.int64)).to(o_nat.device)
+        err, _ = check_output(o_nat[h].index_select(0, sel).float().cpu().numpy(), ro, wl.dtype)
+        r = torch.from_numpy(rows.astype(np.int64)).to(o_nat.device)
+        e_lse = float(np.max(np.abs(L[h].index_select(0, r).cpu().numpy() - rL)))
+        assert e_lse <= LSE_TOL, "head %d lse err %.3g" % (h, e_lse)
+        worst = max(worst, err)
+    say("  natural sparse vs oracle: max-abs %.3g" % worst)
+
+
+@pytest.mark.parametrize("F,H,W,tile,tau", [
+    (3, 15, 20, (8, 8), 0.03),    # ragged last q- and k-block; clipped 7 x 8 and 7 x 4 tiles
+    (3, 21, 24, (6, 12), 0.02),
+    (2, 9, 28, (4, 4), 0.05),
+    (5, 12, 20, (8, 8), 0.002),   # short lists
+    (1, 4, 8, (8, 8), 0.03),      # N = 32: one ragged tile
+])
+def test_natural_sparse_against_oracle(orc, F, H, W, tile, tau):
+    # block lists from the oracle's mask of seeded entropies; every query of both heads
+    torch = torch_mod()
+    t = tra()
+    wl = _wl(500 + F + H + W, F, H, W, tile, tau=tau)
+    say("natural sparse vs oracle", F, H, W, tile, tau)
+    qkv = qkv_inputs(wl)
+    q, k, v = (x.to(device()) for x in qkv)
+    ent = synth.entropy_like(600 + F + H, wl.outer, wl.N)
+    mask = np.stack([orc.block_mask(ent[h], F, H, W, tau, wl.gamma, wl.block_q, wl.block_k, 1, tile[0],
+                                    tile[1])[0] for h in range(wl.outer)])
+    cnt, idx = _lists_from_mask(mask)
+    o, L = t.block_sparse_attn_natural(q, k, v, torch.from_numpy(cnt).to(device()), torch.from_numpy(idx).to(device()),
+                                       F, H, W, wl.block_q, wl.block_k, wl.sm_scale, lse=True, tile_h=tile[0],
+                                       tile_w=tile[1])
+    torch.cuda.synchronize()
+    _check_sparse_natural(orc, wl, qkv, o, L, mask, range(wl.outer), np.arange(wl.nqb))
+
+
+def test_natural_sparse_full_size_against_oracle(orc):
+    # Wan2.1-14B shape: block lists from the GPU mask builder on seeded entropies; seeded q-blocks of
+    # two seeded heads against the oracle's masked attention with its own mask rows of the same
+    # entropies
+    torch = torch_mod()
+    t = tra()
+    wl = workloads.get(3)
+    say("natural sparse vs oracle at full size", wl.name)
+    qkv = qkv_inputs(wl)
+    q, k, v = (x.to(device()) for x in qkv)
+    ent = synth.entropy_like(303, wl.outer, wl.N)
+    cnt, idx, _ = t.build_block_mask(torch.from_numpy(ent).to(device()), wl.F, wl.H, wl.W, wl.tau, wl.gamma,
+                                     wl.block_q, wl.block_k, wl.vote_threshold)
+    t.natural_prepare(wl.F, wl.H, wl.W)
+    o, L = t.block_sparse_attn_natural(q, k, v, cnt, idx, wl.F, wl.H, wl.W, wl.block_q, wl.block_k, wl.sm_scale,
+                                       lse=True)
+    torch.cuda.synchronize()
+    del q, k, v
+    blocks, _ = sample_rows(80, wl.N, wl.block_q, 3)
+    heads = synth.uniform_ints(81, 2, 0, wl.outer)
+    mask = np.zeros((wl.outer, wl.nqb, wl.nkb), dtype=np.uint8)
+    for h in heads:
+        mask[h][blocks], _ = orc.block_mask(ent[h], wl.F, wl.H, wl.W, wl.tau, wl.gamma, wl.block_q, wl.block_k,
+                                            wl.vote_threshold, qblocks=blocks)
+    _check_sparse_natural(orc, wl, qkv, o, L, mask, heads, blocks)
 
 
 def test_natural_against_oracle(orc):
