@@ -193,6 +193,13 @@ def main():
     cnt = torch.empty((wl.outer, wl.nqb), dtype=torch.int32, device=dev)
     idx = torch.empty((wl.outer, wl.nqb, wl.nkb), dtype=torch.int32, device=dev)
     tra.mask_prepare(wl.F, wl.H, wl.W, tau, wl.gamma, wl.block_q, wl.block_k)
+    if wl.W % 4 == 0 and wl.tile_w % 4 == 0:
+        tra.natural_prepare(wl.F, wl.H, wl.W, wl.tile_h, wl.tile_w)
+    # static radial-style mask: head h's queries all take the entropy c_h (the warm-up pass still runs)
+    ent_mask = ent
+    if wl.static_mask:
+        ent_mask = torch.tensor(wl.static_entropy, dtype=torch.float32, device=dev).view(wl.outer, 1).expand(
+            wl.outer, wl.N).contiguous()
     stages = ["permute_qkv", "dense_entropy", "build_mask", "sparse_attn", "unpermute"]
 
     def step(ev=None):
@@ -205,9 +212,7 @@ def main():
         mark(1)
         tra.dense_attn_entropy(qp, kp, vp, wl.sm_scale, entropy=True, out=od, ent_out=ent)
         mark(2)
-        if wl.static_mask:
-            ent.fill_(wl.static_entropy)
-        tra.build_block_mask(ent, wl.F, wl.H, wl.W, tau, wl.gamma, wl.block_q, wl.block_k, wl.vote_threshold,
+        tra.build_block_mask(ent_mask, wl.F, wl.H, wl.W, tau, wl.gamma, wl.block_q, wl.block_k, wl.vote_threshold,
                              kv_count=cnt, kv_index=idx)
         mark(3)
         tra.block_sparse_attn(qp, kp, vp, cnt, idx, wl.block_q, wl.block_k, wl.sm_scale, out=osp)

@@ -10,9 +10,10 @@ reports).  For each workload with a density target:
   - log tau is bisected (a fixed 30 steps) until the oracle's block mask of the sampled
     q-blocks has the target density.
 The headline workload is also calibrated to 9% and 19% (the ends of the range the pages
-report).  The static-mask workload (one entropy value for every query, a radial-style mask)
-bisects that value until the density equals the density its base workload reaches at its
-tau.
+report).  The static-mask workload (a radial-style mask: every query of head h takes one
+entropy value c_h) bisects c_h, head by head, until the static mask's density on that head's
+sampled q-blocks equals the density its base workload's head h reaches there at its tau
+(from the oracle's entropies of that head).
 
 Run from the repository root:  python tests/golden/calibrate_tau.py
 The values are then frozen in entropy_adaptive_sparse_amd/workloads.py.
@@ -45,15 +46,17 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     return ((u + r) & np.uint32(0xFFFF0000)).view(np.float32)
 
 
-def sampled_entropies(wl):
-    """(list of (tile-major entropy vector, q-block sample)) for the sampled heads."""
+def sampled_entropies(wl, heads=None, block_seed=None):
+    """(list of (tile-major entropy vector, q-block sample)) for the sampled heads (default: HEADS
+    seeded heads; q-block samples seeded by block_seed(slot) or 600 + 10 wid + slot)."""
     perm = oracle.tile_major_order(wl.F, wl.H, wl.W, wl.tile_h, wl.tile_w)
-    heads = synth.uniform_ints(500 + wl.wid, HEADS, 0, wl.outer)
+    heads = synth.uniform_ints(500 + wl.wid, HEADS, 0, wl.outer) if heads is None else heads
     q, k, v = synth.qkv(wl.wid, wl.outer, wl.F, wl.H, wl.W, wl.D, wl.t_lo, wl.t_hi, heads=heads)
     out = []
     for s, h in enumerate(heads):
         qt, kt, vt = (oracle.permute(bf16_round(x[s]).astype(np.float64), perm) for x in (q, k, v))
-        blocks = synth.uniform_ints(600 + 10 * wl.wid + s, QBLOCKS, 0, wl.nqb)
+        seed = 600 + 10 * wl.wid + s if block_seed is None else block_seed(h)
+        blocks = synth.uniform_ints(seed, QBLOCKS, 0, wl.nqb)
         rows = np.concatenate([np.arange(b * wl.block_q, min(wl.N, (b + 1) * wl.block_q)) for b in blocks])
         _, ent, _ = oracle.attention(qt, kt, vt, wl.sm_scale, rows=rows.astype(np.int32))
         full = np.zeros(wl.N, dtype=np.float32)
@@ -75,7 +78,7 @@ def density(wl, samples, tau: float) -> float:
     return kept / total
 
 
-def bisect(f, lo: float, hi: float, target: float, increasing: bool = True):
+def bisect_bracket(f, lo: float, hi: float, target: float, increasing: bool = True):
     for _ in range(STEPS):
         mid = 0.5 * (lo + hi)
         above = f(mid) > target
@@ -83,6 +86,11 @@ def bisect(f, lo: float, hi: float, target: float, increasing: bool = True):
             hi = mid
         else:
             lo = mid
+    return lo, hi
+
+
+def bisect(f, lo: float, hi: float, target: float, increasing: bool = True):
+    lo, hi = bisect_bracket(f, lo, hi, target, increasing)
     return 0.5 * (lo + hi)
 
 
@@ -111,22 +119,31 @@ def main():
         extra["%.2f" % target] = {"tau": tau, "density": density(wl3, cache[3], tau)}
     result["workloads"][wl3.name]["density_variants"] = extra
     print(wl3.name, extra, flush=True)
-    # static-mask workload: one entropy value for every query of its base workload's samples
+    # static-mask workload: per head h, one entropy value c_h for every query, matched to the
+    # density head h of the base workload reaches on the same sampled q-blocks
     wl5 = workloads.get(5)
     base = workloads.get(3)
-    samples = cache[3]
     base_tau = result["workloads"][base.name]["tau"]
-    target = density(base, samples, base_tau)
+    per_head = {"tau": base_tau, "qblocks_per_head": QBLOCKS, "static_entropy": [], "density": [], "target": []}
+    for h in range(base.outer):
+        t0 = time.time()
+        [(ent, blocks)] = sampled_entropies(base, heads=[h], block_seed=lambda hh: 700 + hh)
+        target = density(base, [(ent, blocks)], base_tau)
 
-    def dens_c(c):
-        flat = [(np.full(base.N, c, dtype=np.float32), blocks) for _, blocks in samples]
-        return density(wl5, flat, base_tau)
+        def dens_c(c):
+            return density(wl5, [(np.full(base.N, c, dtype=np.float32), blocks)], base_tau)
 
-    c = bisect(dens_c, 0.0, math.log(base.N), target)
-    c = float("%.4g" % c)
-    result["workloads"][wl5.name] = {"tau": base_tau, "static_entropy": c, "density": dens_c(c),
-                                     "target": target}
-    print(wl5.name, result["workloads"][wl5.name], flush=True)
+        # density is a step function of c: of the rounded ends of the final bracket, the one whose
+        # density is closest to the target
+        lo, hi = bisect_bracket(dens_c, 0.0, math.log(base.N), target)
+        cands = sorted({float("%.4g" % lo), float("%.4g" % hi), float("%.4g" % (0.5 * (lo + hi)))})
+        c = min(cands, key=lambda x: (abs(dens_c(x) - target), x))
+        per_head["static_entropy"].append(c)
+        per_head["density"].append(dens_c(c))
+        per_head["target"].append(target)
+        print(wl5.name, "head", h, "c_h", c, "density", per_head["density"][-1], "target", target,
+              "%.1f s" % (time.time() - t0), flush=True)
+    result["workloads"][wl5.name] = per_head
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tau_calibration.json")
     with open(path, "w") as fh:
         json.dump(result, fh, indent=2)

@@ -18,12 +18,15 @@ def test_frozen_tau_matches_calibration():
 
 
 def test_static_mask_workload_matches_calibration():
+    # one entropy constant per head, each matched to the density of the same head of workload 3
     cal = json.load(open(GOLDEN))["workloads"]
     wl = workloads.get(5)
     c = cal[wl.name]
-    assert wl.static_mask and wl.static_entropy == c["static_entropy"] and wl.tau == c["tau"]
-    assert abs(c["density"] - c["target"]) < 0.005
-    assert wl.tau == workloads.get(3).tau
+    assert wl.static_mask and wl.tau == c["tau"] and wl.tau == workloads.get(3).tau
+    assert len(wl.static_entropy) == wl.outer == len(c["static_entropy"])
+    assert list(wl.static_entropy) == c["static_entropy"]
+    for d, t in zip(c["density"], c["target"]):
+        assert abs(d - t) < 0.005
 
 
 def test_density_variants_match_calibration():
