@@ -13,6 +13,7 @@ Functions (names as in the C ABI, without the ``tra_`` prefix):
     dense_attn_entropy_mask (the warm-up pass with the mask builder fused in)
     build_block_mask, mask_prepare, natural_prepare
     block_sparse_attn
+    block_sparse_attn_fp8 (fp8 E4M3 q and k, bf16 v and o)
     dense_attn_entropy_natural, dense_attn_entropy_mask_natural, block_sparse_attn_natural
         (natural-order q, k, v, o; the tile-major map applied inside the kernels' loads and stores)
 """
@@ -25,7 +26,7 @@ import threading
 __all__ = [
     "TraError", "library_path", "load", "tile_major_permute", "tile_major_unpermute", "dense_attn_entropy",
     "dense_attn_entropy_mask", "build_block_mask", "mask_prepare", "natural_prepare", "block_sparse_attn",
-    "dense_attn_entropy_natural", "dense_attn_entropy_mask_natural", "block_sparse_attn_natural",
+    "block_sparse_attn_fp8", "dense_attn_entropy_natural", "dense_attn_entropy_mask_natural", "block_sparse_attn_natural",
     "exported_symbols",
 ]
 
@@ -77,6 +78,7 @@ def load():
         lib.tra_mask_prepare.argtypes = [i32, i32, i32, f32, f32, i32, i32, i32, i32]
         lib.tra_natural_prepare.argtypes = [i32, i32, i32, i32, i32]
         lib.tra_block_sparse_attn.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, f32, i32, i32, P]
+        lib.tra_block_sparse_attn_fp8.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, f32, i32, i32, P]
         lib.tra_dense_attn_entropy_mask.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f32, f32, f32,
                                                     i32, i32, i32, i32, i32, P, P, i64, P, P]
         lib.tra_dense_attn_entropy_mask_natural.argtypes = lib.tra_dense_attn_entropy_mask.argtypes
@@ -86,7 +88,7 @@ def load():
                                                       i32, i32, i32, P]
         for name in ("tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
                      "tra_build_block_mask", "tra_mask_prepare", "tra_natural_prepare", "tra_block_sparse_attn",
-                     "tra_dense_attn_entropy_mask", "tra_dense_attn_entropy_natural",
+                     "tra_block_sparse_attn_fp8", "tra_dense_attn_entropy_mask", "tra_dense_attn_entropy_natural",
                      "tra_block_sparse_attn_natural", "tra_dense_attn_entropy_mask_natural"):
             getattr(lib, name).restype = i32
         _lib = lib
@@ -96,7 +98,7 @@ def load():
 def exported_symbols():
     return ["tra_status_string", "tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
             "tra_build_block_mask", "tra_mask_prepare", "tra_natural_prepare", "tra_block_sparse_attn",
-            "tra_dense_attn_entropy_mask",
+            "tra_block_sparse_attn_fp8", "tra_dense_attn_entropy_mask",
             "tra_dense_attn_entropy_natural", "tra_block_sparse_attn_natural", "tra_dense_attn_entropy_mask_natural"]
 
 
@@ -115,6 +117,17 @@ def _dt(t) -> int:
     if t.dtype == torch.bfloat16:
         return TRA_BF16
     raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+
+
+def _rows(x):
+    """(row_elems, dtype code) under which the permutation moves x's token rows as bytes: fp32 and
+    bf16 as themselves, one-byte types (fp8) as bf16 pairs."""
+    per_row = 1 if x.dim() == 2 else int(x[0, 0].numel())
+    if x.element_size() == 1:
+        if per_row % 2:
+            raise ValueError("one-byte rows must hold an even number of elements")
+        return per_row // 2, TRA_BF16
+    return per_row, _dt(x)
 
 
 def _dev(t, name):
@@ -161,10 +174,10 @@ def tile_major_permute(x, F: int, H: int, W: int, tile_h: int = 8, tile_w: int =
     _dev(x, "x")
     y = _buf(out, "out", x.shape, x.dtype, x)
     outer, N = x.shape[0], x.shape[1]
-    row = 1 if x.dim() == 2 else int(x[0, 0].numel())
+    row, dt = _rows(x)
     if N != F * H * W:
         raise ValueError("x has %d tokens, F*H*W = %d" % (N, F * H * W))
-    _call("tra_tile_major_permute", _ptr(x), _ptr(y), outer, F, H, W, row, _dt(x), tile_h, tile_w, _stream(x))
+    _call("tra_tile_major_permute", _ptr(x), _ptr(y), outer, F, H, W, row, dt, tile_h, tile_w, _stream(x))
     return y
 
 
@@ -173,10 +186,10 @@ def tile_major_unpermute(y, F: int, H: int, W: int, tile_h: int = 8, tile_w: int
     _dev(y, "y")
     x = _buf(out, "out", y.shape, y.dtype, y)
     outer, N = y.shape[0], y.shape[1]
-    row = 1 if y.dim() == 2 else int(y[0, 0].numel())
+    row, dt = _rows(y)
     if N != F * H * W:
         raise ValueError("y has %d tokens, F*H*W = %d" % (N, F * H * W))
-    _call("tra_tile_major_unpermute", _ptr(y), _ptr(x), outer, F, H, W, row, _dt(y), tile_h, tile_w, _stream(y))
+    _call("tra_tile_major_unpermute", _ptr(y), _ptr(x), outer, F, H, W, row, dt, tile_h, tile_w, _stream(y))
     return x
 
 
@@ -292,6 +305,33 @@ def block_sparse_attn(q, k, v, kv_count, kv_index, block_q: int = 128, block_k: 
     scale = (1.0 / D ** 0.5) if sm_scale is None else float(sm_scale)
     _call("tra_block_sparse_attn", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), _ptr(kv_count), _ptr(kv_index),
           outer, N, D, _dt(q), scale, block_q, block_k, _stream(q))
+    return o, L
+
+
+def block_sparse_attn_fp8(q, k, v, kv_count, kv_index, block_q: int = 128, block_k: int = 64,
+                          sm_scale: float | None = None, lse: bool = False, out=None, lse_out=None):
+    """block_sparse_attn with fp8 (OCP E4M3, torch.float8_e4m3fn) q and k and bf16 v; o is bf16.
+    Returns (o, lse)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+        if t.dim() != 3:
+            raise ValueError("%s must be [outer][N][D]" % n)
+    if q.dtype != torch.float8_e4m3fn or k.dtype != torch.float8_e4m3fn or v.dtype != torch.bfloat16:
+        raise ValueError("q and k must be float8_e4m3fn, v bfloat16")
+    if not (q.shape == k.shape == v.shape) or not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must share shape and device")
+    outer, N, D = q.shape
+    nqb, nkb = -(-N // block_q), -(-N // block_k)
+    if kv_count is None or kv_index is None:
+        raise ValueError("kv_count and kv_index are required")
+    _buf(kv_count, "kv_count", (outer, nqb), torch.int32, q)
+    _buf(kv_index, "kv_index", (outer, nqb, nkb), torch.int32, q)
+    o = _buf(out, "out", v.shape, torch.bfloat16, q)
+    L = _buf(lse_out, "lse_out", (outer, N), torch.float32, q) if lse else None
+    scale = (1.0 / D ** 0.5) if sm_scale is None else float(sm_scale)
+    _call("tra_block_sparse_attn_fp8", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), _ptr(kv_count), _ptr(kv_index),
+          outer, N, D, scale, block_q, block_k, _stream(q))
     return o, L
 
 

@@ -37,6 +37,8 @@
 
 #include <hip/hip_bf16.h>
 
+#include <type_traits>
+
 namespace tra {
 
 namespace {
@@ -314,18 +316,20 @@ struct NoCopies {
 // c * NPOS / NC) instead of in one burst at the step's start: a burst holds the wavefront at
 // the vector memory issue path while its matrix instructions wait.  Full tiles only.  The
 // same copies as fetch_tile's: tile-major, ksrc / vsrc are the tiles' first bytes; NAT, they
-// are the head's base and natK / natV hold the tiles' row groups (nat_groups).
-template <int D, int NT, bool NAT>
+// are the head's base and natK / natV hold the tiles' row groups (nat_groups).  K rows hold DK
+// bf16 values' worth of bytes (DK = D/2 for fp8 keys), V rows D bf16 values; NPOS S^T products.
+template <int DK, int DV, int NT, bool NAT, int NPOS>
 struct SpreadCopies {
-    using C = Bf16Cfg<D, NT>;
+    using CK = Bf16Cfg<DK, NT>;
+    using CV = Bf16Cfg<DV, NT>;
     const char *ksrc, *vsrc;
     lds_char_t *kdst, *vdst;
     int soffK, soffV, natK, natV, w;
 
     template <bool ISV>
     __device__ inline void copy(int i) const {
-        const int m = w * C::DMA + i;
-        const int so = (ISV ? soffV : soffK) ^ copy_xor<D, NT, ISV>(m);
+        const int m = w * (ISV ? CV::DMA : CK::DMA) + i;
+        const int so = ISV ? (soffV ^ copy_xor<DV, NT, true>(m)) : (soffK ^ copy_xor<DK, NT, false>(m));
         lds_char_t *dst = (ISV ? vdst : kdst) + m * 1024;
         if constexpr (NAT)
             __builtin_amdgcn_global_load_lds((ISV ? vsrc : ksrc) + lane_offset(lane_value(ISV ? natV : natK, i) + so), dst,
@@ -334,14 +338,14 @@ struct SpreadCopies {
             __builtin_amdgcn_global_load_lds(uniform_ptr((ISV ? vsrc : ksrc) + m * 1024) + lane_offset(so), dst, 16, 0, 0);
     }
     __device__ inline void at(int n) const {
-        constexpr int NPOS = 2 * (D / 16), NC = 2 * C::DMA;
+        constexpr int NC = CK::DMA + CV::DMA;
 #pragma unroll
         for (int c = 0; c < NC; ++c)
             if (c * NPOS / NC == n) {
-                if (c < C::DMA)
+                if (c < CK::DMA)
                     copy<false>(c);
                 else
-                    copy<true>(c - C::DMA);
+                    copy<true>(c - CK::DMA);
             }
     }
 };
@@ -363,6 +367,35 @@ __device__ inline void qk_tile(f32x16_t (&s)[2][QW], const lds_char_t *kb, const
             for (int q2 = 0; q2 < QW; ++q2)
                 s[b][q2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[q2][ks], ks == 0 ? zero : s[b][q2], 0, 0, 0);
             cp.at(b * (D / 16) + ks);
+        }
+    }
+}
+
+// S^T = K Q^T for one 64-key tile with fp8 (OCP e4m3) keys and queries on the fp8 matrix cores
+// (v_mfma_f32_32x32x64_f8f6f4: the 64 products of a step reduce over 64 head dimensions).  LDS
+// holds the K tile as rows of D bytes, 16-byte chunk c of row r at chunk c ^ ((r >> 1) & 7) (the
+// layout of a 128-byte bf16 row).  Lane (ql, h) reads key 32 b + ql, dims 64 ks + 32 h .. + 32
+// (chunks 4 ks + 2 h and 4 ks + 2 h + 1; koff8) and holds the same dims of its query (q8): A and B
+// split the reduction the same way, so the product is the full dot product whatever order the
+// matrix core takes the 32 bytes of a lane in.  cp.at(n) runs after product n.
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+template <int D, class Copies = NoCopies>
+__device__ inline void qk_tile_f8(f32x16_t (&s)[2][1], const lds_char_t *kb, const int (&koff8)[D / 32],
+                                  const i32x8_t (&q8)[D / 64], const Copies &cp = Copies()) {
+    const f32x16_t zero = {};
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int ks = 0; ks < D / 64; ++ks) {
+            typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
+            const u32x4_t lo = *reinterpret_cast<lds_u32x4_t *>(kb + koff8[2 * ks] + b * 32 * D);
+            const u32x4_t hi = *reinterpret_cast<lds_u32x4_t *>(kb + koff8[2 * ks + 1] + b * 32 * D);
+            const i32x8_t av = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            // formats 0, 0: e4m3 for A and B; no block scales (the product is unscaled)
+            s[b][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, q8[ks], ks == 0 ? zero : s[b][0], 0, 0, 0, 0,
+                                                                      0, 0);
+            cp.at(b * (D / 64) + ks);
         }
     }
 }
@@ -417,10 +450,27 @@ __device__ inline float tile_max(const f32x16_t (&s)[2][QW], int q2, float c) {
 // NAT: q, k, v and o are in natural token order and are read and written through the
 // tile-major map (nat4); the entropy and lse stay indexed by tile-major position, and the
 // arithmetic is that of the tile-major kernel on the permuted tensors, bit for bit.
-template <int D, int NW, int QW, bool SPARSE, bool ENT, bool NAT = false>
+// KF8: q and k are fp8 (OCP e4m3, one byte per element), S^T on the fp8 matrix cores (qk_tile_f8);
+// v and o stay bf16 and everything after S^T is unchanged.  K rows are then D bytes: the tile
+// configuration of a D/2-wide bf16 row (DK).
+template <int D, int QW, bool KF8>
+struct QRegs {
+    bf16x8_t qf[QW][D / 16];  // lane holds queries q0 + 32 q2, dims 16 ks + 8 h .. + 8
+};
+template <int D, int QW>
+struct QRegs<D, QW, true> {
+    i32x8_t q8[D / 64];       // lane holds query q0, dims 64 ks + 32 h .. + 32 (fp8)
+};
+
+template <int D, int NW, int QW, bool SPARSE, bool ENT, bool NAT = false, bool KF8 = false>
 struct Bf16Kernel {
     static constexpr int NT = NW * 64;
-    using C = Bf16Cfg<D, NT>;
+    static constexpr int DK = KF8 ? D / 2 : D;   // K row bytes / 2
+    using C = Bf16Cfg<D, NT>;                   // V tiles (and K tiles unless KF8)
+    using CK = Bf16Cfg<DK, NT>;                 // K tiles
+    static_assert(!KF8 || (QW == 1 && !NAT && D == 128), "fp8 keys: one 32-query block per wavefront, D = 128");
+    static constexpr int NPOS = KF8 ? 2 * (D / 64) : 2 * (D / 16);  // S^T products per tile
+    using Spread = SpreadCopies<DK, D, NT, NAT, NPOS>;
 
     struct Ctx {
         const char *kp, *vp;
@@ -431,10 +481,10 @@ struct Bf16Kernel {
         int keyV, keyK;         // fast sparse steps, tile-major: first keys of tiles j + 1, j + 2
         int N, nkb, nfull, ntiles, wave, lane, h;  // nfull: full 64-key tiles, N / 64
         float c;
-        int koff[D / 16];
+        int koff[D / 16];  // K operand offsets (KF8: the first D / 32)
         int voff[D / 32];
         int soffK, soffV;  // lane offset in copy 0 of a K / V tile (copy_xor gives the others)
-        bf16x8_t qf[QW][D / 16];
+        QRegs<D, QW, KF8> qr;
         f32x16_t oacc[D / 32][QW];
         RowState st[QW];
         float mt[QW];  // scaled max of the tile whose scores are current
@@ -452,6 +502,24 @@ struct Bf16Kernel {
         return j * KT;
     }
 
+    // S^T of the tile in kb, with the copies of cp between the products (FAST) or none
+    template <bool FAST>
+    static __device__ inline void qk(const Ctx &x, f32x16_t (&sn)[2][QW], const lds_char_t *kb, const Spread &cp,
+                                     std::integral_constant<bool, FAST>) {
+        if constexpr (KF8) {
+            const int(&k8)[D / 32] = *reinterpret_cast<const int(*)[D / 32]>(&x.koff[0]);
+            if constexpr (FAST)
+                qk_tile_f8<D>(sn, kb, k8, x.qr.q8, cp);
+            else
+                qk_tile_f8<D>(sn, kb, k8, x.qr.q8);
+        } else {
+            if constexpr (FAST)
+                qk_tile<D, NT, QW>(sn, kb, x.koff, x.qr.qf, cp);
+            else
+                qk_tile<D, NT, QW>(sn, kb, x.koff, x.qr.qf);
+        }
+    }
+
     // kn: K_{j+1} (read); kd: buffer receiving K_{j+2}; vc: V_j (read); vd: buffer receiving
     // V_{j+1}; s: S_j; sn: receives S_{j+1} (computed unconditionally: past the last tile it
     // is unused).  Buffers are distinct LDS objects fixed at compile time, so the reads never
@@ -464,18 +532,18 @@ struct Bf16Kernel {
                                        lds_char_t *vd, f32x16_t (&s)[2][QW], f32x16_t (&sn)[2][QW]) {
         int natn = 0;  // NAT: groups of tile j + 3, the K copy of the next step
         if constexpr (NAT) natn = nat_groups<D, NT>(x.nat4v, key0_full(x, min(j + 3, x.ntiles - 1)), x.N, x.wave, x.lane);
-        SpreadCopies<D, NT, NAT> cp{};
+        Spread cp{};
         if constexpr (FAST) {
             const int w = __builtin_amdgcn_readfirstlane(x.wave);
             if constexpr (NAT)
-                cp = SpreadCopies<D, NT, NAT>{x.kp, x.vp, kd, vd, opaque(x.soffK), opaque(x.soffV), x.natK, x.natV, w};
+                cp = Spread{x.kp, x.vp, kd, vd, opaque(x.soffK), opaque(x.soffV), x.natK, x.natV, w};
             else
-                cp = SpreadCopies<D, NT, NAT>{x.kp + (int64_t)(SPARSE ? x.keyK : key0_full(x, j + 2)) * C::ROW,
-                                              x.vp + (int64_t)(SPARSE ? x.keyV : key0_full(x, j + 1)) * C::ROW, kd, vd,
-                                              opaque(x.soffK), opaque(x.soffV), 0, 0, w};
+                cp = Spread{x.kp + (int64_t)(SPARSE ? x.keyK : key0_full(x, j + 2)) * CK::ROW,
+                            x.vp + (int64_t)(SPARSE ? x.keyV : key0_full(x, j + 1)) * C::ROW, kd, vd,
+                            opaque(x.soffK), opaque(x.soffV), 0, 0, w};
         } else {
             if (j + 2 < x.ntiles)
-                fetch_tile<D, NT, false, NAT>(x.kp, x.nat4, x.natK, key0_of(x, j + 2), x.N, kd, x.soffK, x.wave, x.lane);
+                fetch_tile<DK, NT, false, NAT>(x.kp, x.nat4, x.natK, key0_of(x, j + 2), x.N, kd, x.soffK, x.wave, x.lane);
             if (j + 1 < x.ntiles)
                 fetch_tile<D, NT, true, NAT>(x.vp, x.nat4, x.natV, key0_of(x, j + 1), x.N, vd, x.soffV, x.wave, x.lane);
         }
@@ -505,10 +573,7 @@ struct Bf16Kernel {
         // LDS reads, so the K operands are read ahead of their products (measured: 3% faster
         // sparse, dense and fused calls than the default schedule)
         __builtin_amdgcn_iglp_opt(0);
-        if constexpr (FAST)
-            qk_tile<D, NT, QW>(sn, kn, x.koff, x.qf, cp);
-        else
-            qk_tile<D, NT, QW>(sn, kn, x.koff, x.qf);
+        qk(x, sn, kn, cp, std::integral_constant<bool, FAST>());
         float nm[QW], ls[QW], ts[QW];
 #pragma unroll
         for (int q2 = 0; q2 < QW; ++q2) {
@@ -587,8 +652,8 @@ struct Bf16Kernel {
     template <class Epi = NoEpilogue>
     static __device__ void run(const AttnArgs &a, const Epi &epi = Epi()) {
         constexpr int BQ = NW * 32 * QW;
-        __shared__ __attribute__((aligned(1024))) char k0_raw[C::TILE];
-        __shared__ __attribute__((aligned(1024))) char k1_raw[C::TILE];
+        __shared__ __attribute__((aligned(1024))) char k0_raw[CK::TILE];
+        __shared__ __attribute__((aligned(1024))) char k1_raw[CK::TILE];
         __shared__ __attribute__((aligned(1024))) char v0_raw[C::TILE];
         __shared__ __attribute__((aligned(1024))) char v1_raw[C::TILE];
         lds_char_t *K0 = (lds_char_t *)k0_raw, *K1 = (lds_char_t *)k1_raw;
@@ -610,7 +675,8 @@ struct Bf16Kernel {
         x.c = a.c;
         const int64_t head = (int64_t)o * N * D;
         const __bf16 *qp = static_cast<const __bf16 *>(a.q) + head;
-        x.kp = reinterpret_cast<const char *>(static_cast<const __bf16 *>(a.k) + head);
+        // K rows are CK::ROW bytes (D bytes for fp8 keys)
+        x.kp = static_cast<const char *>(a.k) + head * (CK::ROW / D);
         x.vp = reinterpret_cast<const char *>(static_cast<const __bf16 *>(a.v) + head);
         const int q0 = qb * BQ + x.wave * 32 * QW + ql;  // query of block 0 (block q2: + 32 q2)
 
@@ -631,23 +697,45 @@ struct Bf16Kernel {
             if constexpr (NAT) qrow[q2] = qi < N ? natural_row(x.nat4, qi) : qi;
         }
 
-        // Q^T operands: lane holds queries q0 + 32 q2, dims 16 ks + 8 h .. + 8
+        if constexpr (KF8) {
+            // fp8 Q^T operands: lane holds query q0, dims 64 ks + 32 h .. + 32 (one byte each)
+            const char *q8p = static_cast<const char *>(a.q) + head;
 #pragma unroll
-        for (int q2 = 0; q2 < QW; ++q2) {
-            const int qi = q0 + 32 * q2;
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                u32x4_t val = {0u, 0u, 0u, 0u};
-                if (qi < N) val = *reinterpret_cast<const u32x4_t *>(qp + (int64_t)qrow[q2] * D + ks * 16 + h * 8);
-                x.qf[q2][ks] = __builtin_bit_cast(bf16x8_t, val);
+            for (int ks = 0; ks < D / 64; ++ks) {
+                u32x4_t lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+                if (q0 < N) {
+                    const char *src = q8p + (int64_t)qrow[0] * D + 64 * ks + 32 * h;
+                    lo = *reinterpret_cast<const u32x4_t *>(src);
+                    hi = *reinterpret_cast<const u32x4_t *>(src + 16);
+                }
+                x.qr.q8[ks] = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             }
-        }
-        {
+            // K operand: chunks 4 ks + 2 h + part of key ql (+ 32 b), stored at chunk c ^ fK(ql)
+            const int xk = CK::fK(ql);
+#pragma unroll
+            for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+                for (int part = 0; part < 2; ++part)
+                    x.koff[2 * ks + part] = ql * CK::ROW + 16 * ((4 * ks + 2 * h + part) ^ xk);
+        } else {
+            // Q^T operands: lane holds queries q0 + 32 q2, dims 16 ks + 8 h .. + 8
+#pragma unroll
+            for (int q2 = 0; q2 < QW; ++q2) {
+                const int qi = q0 + 32 * q2;
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    u32x4_t val = {0u, 0u, 0u, 0u};
+                    if (qi < N) val = *reinterpret_cast<const u32x4_t *>(qp + (int64_t)qrow[q2] * D + ks * 16 + h * 8);
+                    x.qr.qf[q2][ks] = __builtin_bit_cast(bf16x8_t, val);
+                }
+            }
             // K operand: chunk 2 ks + h of key ql (+ 32 b), stored at chunk (2 ks + h) ^ fK(ql)
             const int xk = C::fK(ql);
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks)
                 x.koff[ks] = ql * C::ROW + 32 * (ks ^ (xk >> 1)) + 16 * (h ^ (xk & 1));
+        }
+        {
             // V^T operand source: key 4 hh + i / 4 (+ 16 s, + 8), dims 32 db + 16 (g % 2) + 4 (i % 4)
             const int g = lane >> 4, i = lane & 15, hh = g >> 1;
             const int u = 2 * (g & 1) + ((i & 3) >> 1);
@@ -660,8 +748,9 @@ struct Bf16Kernel {
         {
             // copy 0's slots: row lane / NCH, chunk lane % NCH; for NAT the row counts within the
             // copy's run of four natural rows, which is the same number
+            const int rk = lane / CK::NCH, pk = lane % CK::NCH;
+            x.soffK = rk * CK::ROW + ((pk ^ CK::fK(rk)) << 4);
             const int row = lane / C::NCH, p = lane % C::NCH;
-            x.soffK = row * C::ROW + ((p ^ C::fK(row)) << 4);
             x.soffV = row * C::ROW + ((p ^ C::fV(row)) << 4);
         }
 
@@ -689,13 +778,13 @@ struct Bf16Kernel {
                 x.natV = nat_groups<D, NT>(x.nat4v, key0_full(x, min(1, x.ntiles - 1)), N, x.wave, lane);
                 x.natK = nat_groups<D, NT>(x.nat4v, key0_full(x, min(2, x.ntiles - 1)), N, x.wave, lane);
             }
-            fetch_tile<D, NT, false, NAT>(x.kp, x.nat4, n0, k0, N, K0, x.soffK, x.wave, lane);
+            fetch_tile<DK, NT, false, NAT>(x.kp, x.nat4, n0, k0, N, K0, x.soffK, x.wave, lane);
             fetch_tile<D, NT, true, NAT>(x.vp, x.nat4, n0, k0, N, V0, x.soffV, x.wave, lane);
             if (x.ntiles > 1)
-                fetch_tile<D, NT, false, NAT>(x.kp, x.nat4, x.natV, key0_of(x, 1), N, K1, x.soffK, x.wave, lane);
+                fetch_tile<DK, NT, false, NAT>(x.kp, x.nat4, x.natV, key0_of(x, 1), N, K1, x.soffK, x.wave, lane);
             wait_dma();
             __syncthreads();
-            qk_tile<D, NT, QW>(s0, K0, x.koff, x.qf);
+            qk(x, s0, K0, Spread{}, std::integral_constant<bool, false>());
 #pragma unroll
             for (int q2 = 0; q2 < QW; ++q2) x.mt[q2] = tile_max<QW>(s0, q2, x.c);
             __syncthreads();  // every wavefront is done with K_0 before K_2 overwrites it
@@ -786,9 +875,9 @@ struct MaskEpilogue {
 // 8-wavefront ones get two per SIMD from a single workgroup, and the 2-wavefront ones
 // (64-query blocks) are held to one per SIMD by their 64 KB of LDS anyway, so those
 // two take the whole register file.
-template <int D, int NW, int QW, bool SPARSE, bool ENT, bool NAT = false>
+template <int D, int NW, int QW, bool SPARSE, bool ENT, bool NAT = false, bool KF8 = false>
 __global__ __launch_bounds__(NW * 64, (QW == 1 && NW == 4) ? 2 : 1) void attn_bf16_kernel(AttnArgs a) {
-    Bf16Kernel<D, NW, QW, SPARSE, ENT, NAT>::run(a);
+    Bf16Kernel<D, NW, QW, SPARSE, ENT, NAT, KF8>::run(a);
 }
 
 // dense attention + entropy + the mask rows of two 128-query blocks per workgroup (D = 128,
@@ -963,6 +1052,12 @@ hipError_t launch_dense_mask(const AttnArgs &a, const MaskArgs &m, hipStream_t s
     b.nqb = (a.N + 255) / 256;  // attention blocks of two mask q-blocks
     const unsigned blocks = (unsigned)((int64_t)b.outer * b.nqb);
     return a.nat4 ? launch_dense_mask_t<true>(b, m, blocks, s) : launch_dense_mask_t<false>(b, m, blocks, s);
+}
+
+hipError_t launch_attention_fp8(const AttnArgs &a, hipStream_t s) {
+    const unsigned blocks = (unsigned)((int64_t)a.outer * a.nqb);
+    attn_bf16_kernel<128, 4, 1, true, false, false, true><<<blocks, 256, 0, s>>>(a);
+    return hipGetLastError();
 }
 
 hipError_t launch_attention_natural(const AttnArgs &a, bool sparse, hipStream_t s) {

@@ -521,6 +521,21 @@ tra_status tra_block_sparse_attn_natural(const void *q, const void *k, const voi
     return from_hip(tra::launch_attention_natural(a, true, s), "sparse attention (natural order)");
 }
 
+tra_status tra_block_sparse_attn_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+                                     const int32_t *kv_count, const int32_t *kv_index, int outer, int N, int D,
+                                     float sm_scale, int block_q, int block_k, hipStream_t s) {
+    // q and k are one byte per element, v and o bf16: the common checks hold for every one
+    tra_status st = check_attn_common(q, k, v, o, outer, N, D, TRA_BF16, sm_scale);
+    if (st != TRA_OK) return st;
+    if (!kv_count || !kv_index) return TRA_ERR_INVALID_ARG;
+    if (block_q < 1 || block_k < 1) return TRA_ERR_INVALID_ARG;
+    if (D != 128 || block_q != 128 || block_k != 64) return TRA_ERR_UNSUPPORTED;
+    tra::AttnArgs a = attn_args(q, k, v, o, nullptr, lse, outer, N, sm_scale);
+    a.kv_count = kv_count; a.kv_index = kv_index;
+    clear_pending_error();
+    return from_hip(tra::launch_attention_fp8(a, s), "sparse attention (fp8 q, k)");
+}
+
 tra_status tra_block_sparse_attn(const void *q, const void *k, const void *v, void *o, float *lse,
                                  const int32_t *kv_count, const int32_t *kv_index, int outer, int N, int D,
                                  tra_dtype dt, float sm_scale, int block_q, int block_k, hipStream_t s) {

@@ -114,6 +114,9 @@ struct AttnArgs {
 // dtype: 0 = fp32, 1 = bf16.  sparse: walk kv_index; else every k-block (dense).
 hipError_t launch_attention(const AttnArgs &a, int D, int dtype, int block_q, bool sparse, hipStream_t s);
 
+// block-sparse attention with fp8 (OCP e4m3) q and k, bf16 v and o: D = 128, 128-query blocks
+hipError_t launch_attention_fp8(const AttnArgs &a, hipStream_t s);
+
 // natural-order q, k, v, o (a.nat4 set): bf16, D = 128; sparse with 128-query blocks
 hipError_t launch_attention_natural(const AttnArgs &a, bool sparse, hipStream_t s);
 

@@ -162,6 +162,28 @@ tra_status tra_block_sparse_attn(const void *q, const void *k, const void *v, vo
                                  tra_dtype dt, float sm_scale, int block_q, int block_k, hipStream_t s);
 
 /*
+ * Block-sparse attention with fp8 queries and keys (section 5: TRA is
+ * complementary to quantization; the reused block-sparse mask of pipeline
+ * step 3 applied to fp8 inputs).  The same result definition as
+ * tra_block_sparse_attn, with the scores taken from fp8 q and k:
+ *
+ *   o_i = sum_{j in retained blocks of q-block(i)} softmax_j(sm_scale <q_i,k_j>) v_j
+ *
+ * q, k: device, [outer][N][D] fp8 in the OCP E4M3 format (one byte per
+ * element: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits; 0x7F and
+ * 0xFF are NaN; no infinities), TILE-MAJOR order.  The scores are computed
+ * on the fp8 matrix cores with fp32 accumulation (the products of two E4M3
+ * values are exact in fp32).  Any quantization scale belongs in sm_scale.
+ * v, o: device, [outer][N][D] bf16.  lse: optional fp32 [outer][N].
+ * kv_count / kv_index as for tra_block_sparse_attn (clamped the same way).
+ * Supported: D = 128, block_q = 128, block_k = 64; anything else returns
+ * TRA_ERR_UNSUPPORTED before any HIP call.
+ */
+tra_status tra_block_sparse_attn_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+                                     const int32_t *kv_count, const int32_t *kv_index, int outer, int N, int D,
+                                     float sm_scale, int block_q, int block_k, hipStream_t s);
+
+/*
  * Warm-up pass with the mask fused in: tra_dense_attn_entropy followed by
  * tra_build_block_mask on its entropies, in one kernel ("Token Radius
  * Attention for Efficient Video Generation", section 2, TRA pipeline: the

@@ -52,6 +52,11 @@ hipError_t launch_attention(const AttnArgs &a, int, int, int, bool, hipStream_t)
     ++g_launches;
     return hipSuccess;
 }
+hipError_t launch_attention_fp8(const AttnArgs &a, hipStream_t) {
+    g_attn = a;
+    ++g_launches;
+    return hipSuccess;
+}
 hipError_t launch_attention_natural(const AttnArgs &a, bool, hipStream_t) {
     g_attn = a;
     ++g_launches;
@@ -211,6 +216,15 @@ int main() {
                                     TRA_BF16, 0.088f, 128, 64, nullptr) == TRA_OK,
               "sparse");
         CHECK(tra_tile_major_permute(q.data(), o.data(), 1, F, H, W, D, TRA_BF16, 8, 8, nullptr) == TRA_OK, "permute");
+        CHECK(tra_block_sparse_attn_fp8(q.data(), k.data(), v.data(), o.data(), nullptr, cnt.data(), idx.data(), 1, N, D,
+                                        0.088f, 128, 64, nullptr) == TRA_OK && g_attn.kv_index == idx.data(),
+              "sparse fp8");
+        CHECK(tra_block_sparse_attn_fp8(q.data(), k.data(), v.data(), o.data(), nullptr, cnt.data(), idx.data(), 1, N, 64,
+                                        0.088f, 128, 64, nullptr) == TRA_ERR_UNSUPPORTED,
+              "sparse fp8, D = 64");
+        CHECK(tra_block_sparse_attn_fp8(q.data(), k.data(), v.data(), o.data(), nullptr, nullptr, idx.data(), 1, N, D,
+                                        0.088f, 128, 64, nullptr) == TRA_ERR_INVALID_ARG,
+              "sparse fp8, no kv_count");
         CHECK(tra_block_sparse_attn(q.data(), k.data(), v.data(), o.data(), nullptr, cnt.data(), idx.data(), 1, N, 96,
                                     TRA_BF16, 0.088f, 128, 64, nullptr) == TRA_ERR_UNSUPPORTED,
               "D = 96");
@@ -218,7 +232,7 @@ int main() {
                                      0.088f, nullptr) == TRA_ERR_INVALID_ARG,
               "null q");
     }
-    CHECK(g_launches == 7, "launch count");
+    CHECK(g_launches == 8, "launch count");
     std::printf("host sanitize ok\n");
     return 0;
 }

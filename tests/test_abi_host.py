@@ -37,7 +37,7 @@ def test_header_declares_the_entry_points():
     for n in ("tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
               "tra_build_block_mask", "tra_block_sparse_attn", "tra_mask_prepare", "tra_status_string",
               "tra_dense_attn_entropy_mask", "tra_dense_attn_entropy_natural", "tra_block_sparse_attn_natural",
-              "tra_dense_attn_entropy_mask_natural", "tra_natural_prepare"):
+              "tra_dense_attn_entropy_mask_natural", "tra_natural_prepare", "tra_block_sparse_attn_fp8"):
         assert n in names
 
 
@@ -197,6 +197,27 @@ def test_natural_order_validation(lib):
     assert call(ff, fused, a11=F32) == UNSUPPORTED                # fp32
     assert call(ff, fused, a7=65, a8=8, a9=8) == UNSUPPORTED      # more frames than the tile buffers hold
     assert call(ff, fused, a22=2 * 8 * 16 - 1) == CAPACITY        # kv_index capacity
+
+
+def test_sparse_fp8_validation(lib):
+    f = lib.tra_block_sparse_attn_fp8
+    # q k v o lse cnt idx outer N D scale bq bk stream
+    base = [FAKE, FAKE2, FAKE3, FAKE4, None, FAKE + 64, FAKE2 + 64, 2, 1024, 128, 0.088, 128, 64, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a0=None) == INVALID              # q
+    assert call(a3=FAKE2) == INVALID             # o aliases k
+    assert call(a5=None) == INVALID              # kv_count
+    assert call(a6=None) == INVALID              # kv_index
+    assert call(a10=0.0) == INVALID              # sm_scale
+    assert call(a9=64) == UNSUPPORTED            # D = 64
+    assert call(a11=64) == UNSUPPORTED           # block_q = 64
+    assert call(a12=32) == UNSUPPORTED           # block_k
+    assert call(a1=FAKE2 + 8) == INVALID         # k not 16-byte aligned
 
 
 def test_natural_prepare_validation(lib):
