@@ -14,6 +14,7 @@ Functions (names as in the C ABI, without the ``tra_`` prefix):
     build_block_mask, mask_prepare, natural_prepare
     block_sparse_attn
     block_sparse_attn_fp8 (fp8 E4M3 q and k, bf16 v and o)
+    sparse_schedule, block_sparse_attn_scheduled (the order the sparse workgroups take the rows in)
     dense_attn_entropy_natural, dense_attn_entropy_mask_natural, block_sparse_attn_natural
         (natural-order q, k, v, o; the tile-major map applied inside the kernels' loads and stores)
 """
@@ -26,7 +27,7 @@ import threading
 __all__ = [
     "TraError", "library_path", "load", "tile_major_permute", "tile_major_unpermute", "dense_attn_entropy",
     "dense_attn_entropy_mask", "build_block_mask", "mask_prepare", "natural_prepare", "block_sparse_attn",
-    "block_sparse_attn_fp8", "dense_attn_entropy_natural", "dense_attn_entropy_mask_natural", "block_sparse_attn_natural",
+    "block_sparse_attn_fp8", "sparse_schedule", "block_sparse_attn_scheduled", "dense_attn_entropy_natural", "dense_attn_entropy_mask_natural", "block_sparse_attn_natural",
     "exported_symbols",
 ]
 
@@ -78,7 +79,9 @@ def load():
         lib.tra_mask_prepare.argtypes = [i32, i32, i32, f32, f32, i32, i32, i32, i32]
         lib.tra_natural_prepare.argtypes = [i32, i32, i32, i32, i32]
         lib.tra_block_sparse_attn.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, f32, i32, i32, P]
-        lib.tra_block_sparse_attn_fp8.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, f32, i32, i32, P]
+        lib.tra_block_sparse_attn_fp8.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, f32, i32, i32, P]
+        lib.tra_sparse_schedule.argtypes = [P, i32, i32, i32, i32, i32, i32, i32, i32, P, i64, P]
+        lib.tra_block_sparse_attn_scheduled.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, f32, i32, i32, P]
         lib.tra_dense_attn_entropy_mask.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, f32, f32, f32,
                                                     i32, i32, i32, i32, i32, P, P, i64, P, P]
         lib.tra_dense_attn_entropy_mask_natural.argtypes = lib.tra_dense_attn_entropy_mask.argtypes
@@ -88,7 +91,8 @@ def load():
                                                       i32, i32, i32, P]
         for name in ("tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
                      "tra_build_block_mask", "tra_mask_prepare", "tra_natural_prepare", "tra_block_sparse_attn",
-                     "tra_block_sparse_attn_fp8", "tra_dense_attn_entropy_mask", "tra_dense_attn_entropy_natural",
+                     "tra_block_sparse_attn_fp8", "tra_sparse_schedule", "tra_block_sparse_attn_scheduled",
+                     "tra_dense_attn_entropy_mask", "tra_dense_attn_entropy_natural",
                      "tra_block_sparse_attn_natural", "tra_dense_attn_entropy_mask_natural"):
             getattr(lib, name).restype = i32
         _lib = lib
@@ -98,7 +102,8 @@ def load():
 def exported_symbols():
     return ["tra_status_string", "tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
             "tra_build_block_mask", "tra_mask_prepare", "tra_natural_prepare", "tra_block_sparse_attn",
-            "tra_block_sparse_attn_fp8", "tra_dense_attn_entropy_mask",
+            "tra_block_sparse_attn_fp8", "tra_sparse_schedule", "tra_block_sparse_attn_scheduled",
+            "tra_dense_attn_entropy_mask",
             "tra_dense_attn_entropy_natural", "tra_block_sparse_attn_natural", "tra_dense_attn_entropy_mask_natural"]
 
 
@@ -309,9 +314,9 @@ def block_sparse_attn(q, k, v, kv_count, kv_index, block_q: int = 128, block_k: 
 
 
 def block_sparse_attn_fp8(q, k, v, kv_count, kv_index, block_q: int = 128, block_k: int = 64,
-                          sm_scale: float | None = None, lse: bool = False, out=None, lse_out=None):
+                          sm_scale: float | None = None, lse: bool = False, out=None, lse_out=None, order=None):
     """block_sparse_attn with fp8 (OCP E4M3, torch.float8_e4m3fn) q and k and bf16 v; o is bf16.
-    Returns (o, lse)."""
+    order: None, or a schedule from sparse_schedule.  Returns (o, lse)."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, n)
@@ -327,11 +332,50 @@ def block_sparse_attn_fp8(q, k, v, kv_count, kv_index, block_q: int = 128, block
         raise ValueError("kv_count and kv_index are required")
     _buf(kv_count, "kv_count", (outer, nqb), torch.int32, q)
     _buf(kv_index, "kv_index", (outer, nqb, nkb), torch.int32, q)
+    if order is not None:
+        _buf(order, "order", (outer * nqb,), torch.int32, q)
     o = _buf(out, "out", v.shape, torch.bfloat16, q)
     L = _buf(lse_out, "lse_out", (outer, N), torch.float32, q) if lse else None
     scale = (1.0 / D ** 0.5) if sm_scale is None else float(sm_scale)
     _call("tra_block_sparse_attn_fp8", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), _ptr(kv_count), _ptr(kv_index),
-          outer, N, D, scale, block_q, block_k, _stream(q))
+          _ptr(order), outer, N, D, scale, block_q, block_k, _stream(q))
+    return o, L
+
+
+def sparse_schedule(kv_count, F: int, H: int, W: int, block_q: int = 128, block_k: int = 64, tile_h: int = 8,
+                    tile_w: int = 8, out=None):
+    """The order the block-sparse calls take the (head, q-block) rows in: int32 [outer * nqb]
+    (longest first for short grids, the spatial band order otherwise)."""
+    torch = _torch()
+    _dev(kv_count, "kv_count")
+    if kv_count.dtype != torch.int32 or kv_count.dim() != 2:
+        raise ValueError("kv_count must be int32 [outer][nqb]")
+    outer, nqb = kv_count.shape
+    if nqb != -(-(F * H * W) // block_q):
+        raise ValueError("kv_count has %d q-blocks, the grid %d" % (nqb, -(-(F * H * W) // block_q)))
+    order = _buf(out, "out", (outer * nqb,), torch.int32, kv_count)
+    _call("tra_sparse_schedule", _ptr(kv_count), outer, F, H, W, block_q, block_k, tile_h, tile_w, _ptr(order),
+          order.numel(), _stream(kv_count))
+    return order
+
+
+def block_sparse_attn_scheduled(q, k, v, kv_count, kv_index, order, block_q: int = 128, block_k: int = 64,
+                                sm_scale: float | None = None, lse: bool = False, out=None, lse_out=None):
+    """block_sparse_attn with the workgroups taking the rows in `order` (from sparse_schedule);
+    the same results bit for bit.  Returns (o, lse)."""
+    torch = _torch()
+    outer, N, D = _check_qkv(q, k, v)
+    nqb, nkb = -(-N // block_q), -(-N // block_k)
+    if kv_count is None or kv_index is None or order is None:
+        raise ValueError("kv_count, kv_index and order are required")
+    _buf(kv_count, "kv_count", (outer, nqb), torch.int32, q)
+    _buf(kv_index, "kv_index", (outer, nqb, nkb), torch.int32, q)
+    _buf(order, "order", (outer * nqb,), torch.int32, q)
+    o = _buf(out, "out", q.shape, q.dtype, q)
+    L = _buf(lse_out, "lse_out", (outer, N), torch.float32, q) if lse else None
+    scale = (1.0 / D ** 0.5) if sm_scale is None else float(sm_scale)
+    _call("tra_block_sparse_attn_scheduled", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), _ptr(kv_count),
+          _ptr(kv_index), _ptr(order), outer, N, D, _dt(q), scale, block_q, block_k, _stream(q))
     return o, L
 
 

@@ -69,6 +69,16 @@ __device__ inline int xcd_remap(int bid, int total) {
     return (k / kXcdChunk) * (8 * kXcdChunk) + x * kXcdChunk + (k % kXcdChunk);
 }
 
+// The (head, q-block) row workgroup b runs: order[b] when the caller passes a schedule (clamped,
+// so any value stays in bounds), else the XCD order above.
+__device__ inline int row_of_workgroup(const AttnArgs &a, int b, int total) {
+    if (a.order) {
+        const int r = ((const int32_t __attribute__((address_space(4))) *)a.order)[b];
+        return min(max(r, 0), total - 1);
+    }
+    return xcd_remap(b, total);
+}
+
 // Lane l and lane l ^ 32 hold the two halves of one query's keys.  v_permlane32_swap on two
 // copies of v leaves {v[l], v[l ^ 32]} in the two results of every lane.  The results are
 // copied to scalars before the bit cast: a bit cast applied directly to an element of the
@@ -665,7 +675,7 @@ struct Bf16Kernel {
         x.wave = tid >> 6;
         x.h = x.lane >> 5;
         const int ql = x.lane & 31, h = x.h, lane = x.lane;
-        const int bid = xcd_remap(blockIdx.x, gridDim.x);
+        const int bid = row_of_workgroup(a, blockIdx.x, gridDim.x);
         const int o = bid / a.nqb;
         const int qb = bid - o * a.nqb;
         const int N = a.N;
@@ -914,7 +924,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_f32_kernel(AttnArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, ql = lane & 31;
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int bid = row_of_workgroup(a, blockIdx.x, gridDim.x);
     const int o = bid / a.nqb;
     const int qb = bid - o * a.nqb;
     const int N = a.N;

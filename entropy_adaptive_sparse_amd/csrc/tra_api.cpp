@@ -267,6 +267,81 @@ tra_status get_nat_table(const TileGeom &g, const int32_t *&out) {
     return TRA_OK;
 }
 
+// ------------------------------------------------------------------ schedule tables
+// band[rank] = the q-block of one head at rank `rank` of the spatial band order: q-blocks sorted by
+// (row of tiles, frame, position along the row of tiles) of their centre token, then by index.
+struct BandKey {
+    int dev, F, H, W, bq, th, tw;
+    bool operator<(const BandKey &o) const {
+        return std::tie(dev, F, H, W, bq, th, tw) < std::tie(o.dev, o.F, o.H, o.W, o.bq, o.th, o.tw);
+    }
+};
+std::map<BandKey, void *> g_band;
+std::map<int, int> g_cus;  // device -> compute units
+
+tra_status get_band_table(const TileGeom &g, int bq, const int32_t *&out) {
+    int dev = 0;
+    const hipError_t de = hipGetDevice(&dev);
+    if (de != hipSuccess) return from_hip(de, "hipGetDevice");
+    const BandKey key{dev, g.F, g.H, g.W, bq, g.th, g.tw};
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_band.find(key);
+    if (it != g_band.end()) {
+        out = static_cast<const int32_t *>(it->second);
+        return TRA_OK;
+    }
+    const int nqb = (g.N + bq - 1) / bq;
+    std::vector<std::tuple<int, int, int, int>> keys;
+    std::vector<int32_t> band;
+    try {
+        keys.reserve((size_t)nqb);
+        band.resize((size_t)nqb);
+    } catch (const std::bad_alloc &) {
+        return TRA_ERR_CAPACITY;
+    }
+    const int span = g.th * g.W;  // tokens in one full row of tiles
+    for (int qb = 0; qb < nqb; ++qb) {
+        const int p0 = std::min(qb * bq + bq / 2, g.N - 1);
+        const int f = p0 / g.HW, r = p0 - f * g.HW;
+        keys.emplace_back(r / span, f, r % span, qb);
+    }
+    std::sort(keys.begin(), keys.end());
+    for (int i = 0; i < nqb; ++i) band[(size_t)i] = std::get<3>(keys[(size_t)i]);
+    void *mem = nullptr;
+    const hipError_t me = hipMalloc(&mem, band.size() * sizeof(int32_t));
+    if (me != hipSuccess) return from_hip(me, "hipMalloc of the band order");
+    const hipError_t ce = hipMemcpy(mem, band.data(), band.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+    if (ce != hipSuccess) {
+        (void)hipFree(mem);
+        return from_hip(ce, "upload of the band order");
+    }
+    g_band.emplace(key, mem);
+    out = static_cast<const int32_t *>(mem);
+    return TRA_OK;
+}
+
+tra_status compute_units(int &cus) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return from_hip(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_cus.find(dev);
+    if (it == g_cus.end()) {
+        int n = 0;
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return from_hip(e, "hipDeviceGetAttribute");
+        it = g_cus.emplace(dev, std::max(1, n)).first;
+    }
+    cus = it->second;
+    return TRA_OK;
+}
+
+// Grids of fewer than this many waves of resident sparse workgroups (two per compute unit) take the
+// longest-first order: there the tail of unequal rows is a sizeable part of the call.
+constexpr int kLptWaves = 16;
+// Largest nkb the longest-first sort holds in its LDS histogram.
+constexpr int kLptMaxBins = 16383;
+
 // Checks shared by the natural-order attention entry points (after check_attn_common).
 tra_status check_natural(int F, int H, int W, int D, tra_dtype dt, int tile_h, int tile_w, TileGeom &g) {
     const tra_status st = check_grid(F, H, W, tile_h, tile_w, g);
@@ -521,9 +596,52 @@ tra_status tra_block_sparse_attn_natural(const void *q, const void *k, const voi
     return from_hip(tra::launch_attention_natural(a, true, s), "sparse attention (natural order)");
 }
 
+tra_status tra_sparse_schedule(const int32_t *kv_count, int outer, int F, int H, int W, int block_q, int block_k,
+                               int tile_h, int tile_w, int32_t *order, int64_t order_capacity, hipStream_t s) {
+    if (!kv_count || !order || outer < 1) return TRA_ERR_INVALID_ARG;
+    TileGeom g;
+    tra_status st = check_grid(F, H, W, tile_h, tile_w, g);
+    if (st != TRA_OK) return st;
+    if (block_q < 1 || block_k < 1) return TRA_ERR_INVALID_ARG;
+    if ((block_q != 64 && block_q != 128) || block_k != 64) return TRA_ERR_UNSUPPORTED;
+    const int nqb = (g.N + block_q - 1) / block_q, nkb = (g.N + block_k - 1) / block_k;
+    if ((int64_t)outer * nqb > ((int64_t)1 << 31) - 1) return TRA_ERR_UNSUPPORTED;
+    if (order_capacity < (int64_t)outer * nqb) return TRA_ERR_CAPACITY;
+    int cus = 0;
+    st = compute_units(cus);
+    if (st != TRA_OK) return st;
+    tra::ScheduleArgs a{};
+    a.kv_count = kv_count; a.order = order;
+    a.outer = outer; a.nqb = nqb; a.nkb = nkb;
+    a.lpt = (int64_t)outer * nqb < (int64_t)kLptWaves * 2 * cus && nkb <= kLptMaxBins;
+    if (!a.lpt) {
+        st = get_band_table(g, block_q, a.band);
+        if (st != TRA_OK) return st;
+    }
+    clear_pending_error();
+    return from_hip(tra::launch_schedule(a, s), "sparse schedule");
+}
+
+tra_status tra_block_sparse_attn_scheduled(const void *q, const void *k, const void *v, void *o, float *lse,
+                                           const int32_t *kv_count, const int32_t *kv_index, const int32_t *order,
+                                           int outer, int N, int D, tra_dtype dt, float sm_scale, int block_q,
+                                           int block_k, hipStream_t s) {
+    tra_status st = check_attn_common(q, k, v, o, outer, N, D, dt, sm_scale);
+    if (st != TRA_OK) return st;
+    if (!kv_count || !kv_index || !order) return TRA_ERR_INVALID_ARG;
+    if (block_q < 1 || block_k < 1) return TRA_ERR_INVALID_ARG;
+    if ((block_q != 64 && block_q != 128) || block_k != 64) return TRA_ERR_UNSUPPORTED;
+    tra::AttnArgs a = attn_args(q, k, v, o, nullptr, lse, outer, N, sm_scale);
+    a.kv_count = kv_count; a.kv_index = kv_index; a.order = order;
+    a.nqb = (N + block_q - 1) / block_q;
+    clear_pending_error();
+    return from_hip(tra::launch_attention(a, D, dt == TRA_BF16 ? 1 : 0, block_q, true, s), "sparse attention (scheduled)");
+}
+
 tra_status tra_block_sparse_attn_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
-                                     const int32_t *kv_count, const int32_t *kv_index, int outer, int N, int D,
-                                     float sm_scale, int block_q, int block_k, hipStream_t s) {
+                                     const int32_t *kv_count, const int32_t *kv_index, const int32_t *order,
+                                     int outer, int N, int D, float sm_scale, int block_q, int block_k,
+                                     hipStream_t s) {
     // q and k are one byte per element, v and o bf16: the common checks hold for every one
     tra_status st = check_attn_common(q, k, v, o, outer, N, D, TRA_BF16, sm_scale);
     if (st != TRA_OK) return st;
@@ -531,7 +649,7 @@ tra_status tra_block_sparse_attn_fp8(const void *q, const void *k, const void *v
     if (block_q < 1 || block_k < 1) return TRA_ERR_INVALID_ARG;
     if (D != 128 || block_q != 128 || block_k != 64) return TRA_ERR_UNSUPPORTED;
     tra::AttnArgs a = attn_args(q, k, v, o, nullptr, lse, outer, N, sm_scale);
-    a.kv_count = kv_count; a.kv_index = kv_index;
+    a.kv_count = kv_count; a.kv_index = kv_index; a.order = order;
     clear_pending_error();
     return from_hip(tra::launch_attention_fp8(a, s), "sparse attention (fp8 q, k)");
 }

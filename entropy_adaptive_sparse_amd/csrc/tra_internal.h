@@ -102,6 +102,9 @@ struct AttnArgs {
     void *o;
     float *ent, *lse;
     const int32_t *kv_count, *kv_index;
+    // null: workgroups take the rows in the library's default order; otherwise workgroup b runs row
+    // order[b] (clamped into [0, outer * nqb)), the order tra_sparse_schedule writes
+    const int32_t *order;
     int outer, N, nqb, nkb;
     float c;          // sm_scale * log2(e)
     float sm_scale;
@@ -113,6 +116,19 @@ struct AttnArgs {
 
 // dtype: 0 = fp32, 1 = bf16.  sparse: walk kv_index; else every k-block (dense).
 hipError_t launch_attention(const AttnArgs &a, int D, int dtype, int block_q, bool sparse, hipStream_t s);
+
+// ---------------------------------------------------------------- schedule
+// Rows per run of the spatial band order on one XCD (about the workgroups an XCD holds at once).
+constexpr int kBandRun = 64;
+
+struct ScheduleArgs {
+    const int32_t *kv_count;  // [outer][nqb] (longest-first order)
+    const int32_t *band;      // [nqb]: one head's q-blocks in band order (band order)
+    int32_t *order;           // [outer * nqb] out
+    int outer, nqb, nkb;
+    bool lpt;                 // longest first; else the spatial band order
+};
+hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s);
 
 // block-sparse attention with fp8 (OCP e4m3) q and k, bf16 v and o: D = 128, 128-query blocks
 hipError_t launch_attention_fp8(const AttnArgs &a, hipStream_t s);

@@ -175,13 +175,52 @@ tra_status tra_block_sparse_attn(const void *q, const void *k, const void *v, vo
  * on the fp8 matrix cores with fp32 accumulation (the products of two E4M3
  * values are exact in fp32).  Any quantization scale belongs in sm_scale.
  * v, o: device, [outer][N][D] bf16.  lse: optional fp32 [outer][N].
- * kv_count / kv_index as for tra_block_sparse_attn (clamped the same way).
+ * kv_count / kv_index as for tra_block_sparse_attn (clamped the same way);
+ * order: NULL, or a schedule from tra_sparse_schedule (as in
+ * tra_block_sparse_attn_scheduled).
  * Supported: D = 128, block_q = 128, block_k = 64; anything else returns
  * TRA_ERR_UNSUPPORTED before any HIP call.
  */
 tra_status tra_block_sparse_attn_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
-                                     const int32_t *kv_count, const int32_t *kv_index, int outer, int N, int D,
-                                     float sm_scale, int block_q, int block_k, hipStream_t s);
+                                     const int32_t *kv_count, const int32_t *kv_index, const int32_t *order,
+                                     int outer, int N, int D, float sm_scale, int block_q, int block_k,
+                                     hipStream_t s);
+
+/*
+ * The order in which the block-sparse calls take the (head, q-block) rows
+ * (section 4: 9-19% of the interactions are kept, and the per-query budgets
+ * differ by orders of magnitude, so the rows' k-block lists -- their work --
+ * differ in length).  Writes order[outer * nqb], a permutation of the rows
+ * o * nqb + qb, for tra_block_sparse_attn_scheduled and
+ * tra_block_sparse_attn_fp8, computed once per mask like kv_index:
+ *  - when the grid is fewer than 16 waves of resident workgroups (two per
+ *    compute unit): longest first, rows sorted by kv_count, largest first,
+ *    ties by row (a list-scheduling order: the shortest rows end the grid);
+ *  - otherwise: the spatial band order, within each head the q-blocks sorted
+ *    by (row of tiles, frame, position along the row of tiles) of their
+ *    centre token, dealt to the 8 XCDs in runs of 64 rows, so that the rows an
+ *    XCD holds at once share most of their k-blocks in its L2.
+ * Either way results are those of tra_block_sparse_attn bit for bit; only the
+ * time changes.  kv_count: device int32 [outer][nqb] (read for the first
+ * order); order: device int32, order_capacity elements (fewer than
+ * outer * nqb returns TRA_ERR_CAPACITY).  block_q in {64, 128}, block_k = 64.
+ * The first call for a geometry builds and uploads the band table
+ * (nqb int32) synchronously; it stays in the per-device cache.
+ */
+tra_status tra_sparse_schedule(const int32_t *kv_count, int outer, int F, int H, int W, int block_q, int block_k,
+                               int tile_h, int tile_w, int32_t *order, int64_t order_capacity, hipStream_t s);
+
+/*
+ * tra_block_sparse_attn with workgroup b running the row order[b] (a schedule
+ * written by tra_sparse_schedule for the same kv_count, outer, N, block_q).
+ * Results equal tra_block_sparse_attn's bit for bit.  order must be a
+ * permutation of [0, outer * nqb); other values are clamped into that range
+ * (every access stays in bounds, but rows may then be left unwritten).
+ */
+tra_status tra_block_sparse_attn_scheduled(const void *q, const void *k, const void *v, void *o, float *lse,
+                                           const int32_t *kv_count, const int32_t *kv_index, const int32_t *order,
+                                           int outer, int N, int D, tra_dtype dt, float sm_scale, int block_q,
+                                           int block_k, hipStream_t s);
 
 /*
  * Warm-up pass with the mask fused in: tra_dense_attn_entropy followed by

@@ -33,6 +33,10 @@ hipError_t hipMemcpy(void *dst, const void *src, size_t n, hipMemcpyKind) {
     return hipSuccess;
 }
 hipError_t hipGetLastError(void) { return hipSuccess; }
+hipError_t hipDeviceGetAttribute(int *v, hipDeviceAttribute_t, int) {
+    *v = 256;
+    return hipSuccess;
+}
 const char *hipGetErrorString(hipError_t) { return "stand-in"; }
 }
 
@@ -40,6 +44,7 @@ namespace {
 int g_launches = 0;
 tra::MaskArgs g_mask;
 tra::AttnArgs g_attn;
+tra::ScheduleArgs g_sched;
 }  // namespace
 
 namespace tra {
@@ -49,6 +54,12 @@ hipError_t launch_permute(const void *, void *, int, const TileGeom &, int64_t, 
 }
 hipError_t launch_attention(const AttnArgs &a, int, int, int, bool, hipStream_t) {
     g_attn = a;
+    ++g_launches;
+    return hipSuccess;
+}
+
+hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t) {
+    g_sched = a;
     ++g_launches;
     return hipSuccess;
 }
@@ -216,15 +227,30 @@ int main() {
                                     TRA_BF16, 0.088f, 128, 64, nullptr) == TRA_OK,
               "sparse");
         CHECK(tra_tile_major_permute(q.data(), o.data(), 1, F, H, W, D, TRA_BF16, 8, 8, nullptr) == TRA_OK, "permute");
-        CHECK(tra_block_sparse_attn_fp8(q.data(), k.data(), v.data(), o.data(), nullptr, cnt.data(), idx.data(), 1, N, D,
-                                        0.088f, 128, 64, nullptr) == TRA_OK && g_attn.kv_index == idx.data(),
+        CHECK(tra_block_sparse_attn_fp8(q.data(), k.data(), v.data(), o.data(), nullptr, cnt.data(), idx.data(), nullptr,
+                                        1, N, D, 0.088f, 128, 64, nullptr) == TRA_OK && g_attn.kv_index == idx.data(),
               "sparse fp8");
-        CHECK(tra_block_sparse_attn_fp8(q.data(), k.data(), v.data(), o.data(), nullptr, cnt.data(), idx.data(), 1, N, 64,
-                                        0.088f, 128, 64, nullptr) == TRA_ERR_UNSUPPORTED,
+        CHECK(tra_block_sparse_attn_fp8(q.data(), k.data(), v.data(), o.data(), nullptr, cnt.data(), idx.data(), nullptr,
+                                        1, N, 64, 0.088f, 128, 64, nullptr) == TRA_ERR_UNSUPPORTED,
               "sparse fp8, D = 64");
-        CHECK(tra_block_sparse_attn_fp8(q.data(), k.data(), v.data(), o.data(), nullptr, nullptr, idx.data(), 1, N, D,
-                                        0.088f, 128, 64, nullptr) == TRA_ERR_INVALID_ARG,
+        CHECK(tra_block_sparse_attn_fp8(q.data(), k.data(), v.data(), o.data(), nullptr, nullptr, idx.data(), nullptr,
+                                        1, N, D, 0.088f, 128, 64, nullptr) == TRA_ERR_INVALID_ARG,
               "sparse fp8, no kv_count");
+        // schedules: a short grid takes the longest-first order, a long one the band order
+        std::vector<int32_t> order(nqb);
+        CHECK(tra_sparse_schedule(cnt.data(), 1, F, H, W, 128, 64, 8, 8, order.data(), nqb, nullptr) == TRA_OK &&
+                  g_sched.lpt && g_sched.nqb == nqb && g_sched.nkb == nkb,
+              "schedule (longest first)");
+        CHECK(tra_sparse_schedule(cnt.data(), 1, F, H, W, 128, 64, 8, 8, order.data(), nqb - 1, nullptr) ==
+                  TRA_ERR_CAPACITY,
+              "schedule capacity");
+        CHECK(tra_block_sparse_attn_scheduled(q.data(), k.data(), v.data(), o.data(), nullptr, cnt.data(), idx.data(),
+                                              order.data(), 1, N, D, TRA_BF16, 0.088f, 128, 64, nullptr) == TRA_OK &&
+                  g_attn.order == order.data(),
+              "scheduled sparse");
+        CHECK(tra_block_sparse_attn_scheduled(q.data(), k.data(), v.data(), o.data(), nullptr, cnt.data(), idx.data(),
+                                              nullptr, 1, N, D, TRA_BF16, 0.088f, 128, 64, nullptr) == TRA_ERR_INVALID_ARG,
+              "scheduled sparse without an order");
         CHECK(tra_block_sparse_attn(q.data(), k.data(), v.data(), o.data(), nullptr, cnt.data(), idx.data(), 1, N, 96,
                                     TRA_BF16, 0.088f, 128, 64, nullptr) == TRA_ERR_UNSUPPORTED,
               "D = 96");
@@ -232,7 +258,27 @@ int main() {
                                      0.088f, nullptr) == TRA_ERR_INVALID_ARG,
               "null q");
     }
-    CHECK(g_launches == 8, "launch count");
+        // a long grid (21 x 45 x 80, 40 heads) takes the spatial band order: the table is a permutation of
+    // one head's q-blocks, ordered by (row of tiles, frame, position along it)
+    {
+        const int F = 21, H = 45, W = 80, N = F * H * W, nqb = (N + 127) / 128, outer = 40;
+        std::vector<int32_t> cnt((size_t)outer * nqb, 5), order((size_t)outer * nqb);
+        CHECK(tra_sparse_schedule(cnt.data(), outer, F, H, W, 128, 64, 8, 8, order.data(), (int64_t)order.size(),
+                                  nullptr) == TRA_OK && !g_sched.lpt && g_sched.band != nullptr,
+              "schedule (band)");
+        std::vector<int> seen(nqb, 0);
+        int prev_band = -1, prev_frame = -1;
+        for (int r = 0; r < nqb; ++r) {
+            const int qb = g_sched.band[r];
+            CHECK(qb >= 0 && qb < nqb && !seen[qb], "band table is a permutation");
+            seen[qb] = 1;
+            const int p0 = std::min(qb * 128 + 64, N - 1), f = p0 / (H * W), band = (p0 % (H * W)) / (8 * W);
+            CHECK(band > prev_band || (band == prev_band && f >= prev_frame), "band table order");
+            prev_band = band;
+            prev_frame = f;
+        }
+    }
+    CHECK(g_launches == 11, "launch count");
     std::printf("host sanitize ok\n");
     return 0;
 }

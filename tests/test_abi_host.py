@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
     for n in ("tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
               "tra_build_block_mask", "tra_block_sparse_attn", "tra_mask_prepare", "tra_status_string",
               "tra_dense_attn_entropy_mask", "tra_dense_attn_entropy_natural", "tra_block_sparse_attn_natural",
-              "tra_dense_attn_entropy_mask_natural", "tra_natural_prepare", "tra_block_sparse_attn_fp8"):
+              "tra_dense_attn_entropy_mask_natural", "tra_natural_prepare", "tra_block_sparse_attn_fp8",
+              "tra_sparse_schedule", "tra_block_sparse_attn_scheduled"):
         assert n in names
 
 
@@ -201,8 +202,8 @@ def test_natural_order_validation(lib):
 
 def test_sparse_fp8_validation(lib):
     f = lib.tra_block_sparse_attn_fp8
-    # q k v o lse cnt idx outer N D scale bq bk stream
-    base = [FAKE, FAKE2, FAKE3, FAKE4, None, FAKE + 64, FAKE2 + 64, 2, 1024, 128, 0.088, 128, 64, None]
+    # q k v o lse cnt idx order outer N D scale bq bk stream
+    base = [FAKE, FAKE2, FAKE3, FAKE4, None, FAKE + 64, FAKE2 + 64, None, 2, 1024, 128, 0.088, 128, 64, None]
 
     def call(**kw):
         a = list(base)
@@ -213,11 +214,37 @@ def test_sparse_fp8_validation(lib):
     assert call(a3=FAKE2) == INVALID             # o aliases k
     assert call(a5=None) == INVALID              # kv_count
     assert call(a6=None) == INVALID              # kv_index
-    assert call(a10=0.0) == INVALID              # sm_scale
-    assert call(a9=64) == UNSUPPORTED            # D = 64
-    assert call(a11=64) == UNSUPPORTED           # block_q = 64
-    assert call(a12=32) == UNSUPPORTED           # block_k
+    assert call(a11=0.0) == INVALID              # sm_scale
+    assert call(a10=64) == UNSUPPORTED           # D = 64
+    assert call(a12=64) == UNSUPPORTED           # block_q = 64
+    assert call(a13=32) == UNSUPPORTED           # block_k
     assert call(a1=FAKE2 + 8) == INVALID         # k not 16-byte aligned
+
+
+def test_schedule_validation(lib):
+    f = lib.tra_sparse_schedule
+    # cnt outer F H W bq bk th tw order cap stream
+    base = [FAKE, 2, 4, 16, 16, 128, 64, 8, 8, FAKE2, 2 * 8, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a0=None) == INVALID              # kv_count
+    assert call(a9=None) == INVALID              # order
+    assert call(a1=0) == INVALID                 # outer
+    assert call(a2=0) == INVALID                 # F
+    assert call(a5=32) == UNSUPPORTED            # block_q
+    assert call(a6=128) == UNSUPPORTED           # block_k
+    assert call(a10=15) == CAPACITY              # order capacity
+    g = lib.tra_block_sparse_attn_scheduled
+    # q k v o lse cnt idx order outer N D dt scale bq bk stream
+    sb = [FAKE, FAKE2, FAKE3, FAKE4, None, FAKE + 64, FAKE2 + 64, FAKE3 + 64, 2, 1024, 128, BF16, 0.088, 128, 64, None]
+    a = list(sb); a[7] = None; assert g(*a) == INVALID       # order
+    a = list(sb); a[6] = None; assert g(*a) == INVALID       # kv_index
+    a = list(sb); a[14] = 32; assert g(*a) == UNSUPPORTED    # block_k
+    a = list(sb); a[10] = 96; assert g(*a) == UNSUPPORTED    # D
 
 
 def test_natural_prepare_validation(lib):

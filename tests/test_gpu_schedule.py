@@ -1,0 +1,110 @@
+"""GPU: the order of the block-sparse workgroups (tra_sparse_schedule; "Token Radius Attention for
+Efficient Video Generation", section 4: 9-19% of the interactions kept with per-query budgets that
+differ by orders of magnitude, hence rows of unequal work).
+
+The schedule only moves work between workgroups: the scheduled calls equal the unscheduled ones bit
+for bit (those are pinned to the oracle in test_gpu_attention.py and test_gpu_fp8.py).  The orders
+themselves are checked against their definitions: a permutation of the rows; longest first by
+kv_count with ties by row for short grids; for long grids the spatial band order dealt to the 8
+XCDs in runs of 64.
+"""
+import numpy as np
+import pytest
+
+from entropy_adaptive_sparse_amd import synth, workloads
+from gpu_util import device, qkv_inputs, say, small_workload, torch_mod, tra
+
+pytestmark = pytest.mark.gpu
+
+RUN = 64
+
+
+def _band_reference(F, H, W, bq, outer, th=8, tw=8):
+    """the documented band order, written out here: per head, q-blocks sorted by (row of tiles,
+    frame, position along the row of tiles) of their centre token, then dealt to XCD b mod 8 in runs"""
+    N = F * H * W
+    nqb = -(-N // bq)
+    keys = []
+    for qb in range(nqb):
+        p0 = min(qb * bq + bq // 2, N - 1)
+        f, r = divmod(p0, H * W)
+        keys.append((r // (th * W), f, r % (th * W), qb))
+    band = [k[3] for k in sorted(keys)]
+    total = outer * nqb
+    full = (total // (8 * RUN)) * (8 * RUN)
+    order = np.empty(total, dtype=np.int64)
+    for b in range(total):
+        if b < full:
+            x, k = b & 7, b >> 3
+            L = (k // RUN) * (8 * RUN) + x * RUN + (k % RUN)
+        else:
+            L = b
+        o, r = divmod(L, nqb)
+        order[b] = o * nqb + band[r]
+    return order
+
+
+def _compare_scheduled(t, wl, qp, kp, vp, cnt, idx, order):
+    torch = torch_mod()
+    o1, l1 = t.block_sparse_attn(qp, kp, vp, cnt, idx, wl.block_q, wl.block_k, wl.sm_scale, lse=True)
+    o2, l2 = t.block_sparse_attn_scheduled(qp, kp, vp, cnt, idx, order, wl.block_q, wl.block_k, wl.sm_scale, lse=True)
+    torch.cuda.synchronize()
+    bits = (lambda x: x.view(torch.int16)) if qp.dtype == torch.bfloat16 else (lambda x: x)
+    assert torch.equal(bits(o1), bits(o2)) and torch.equal(l1, l2), "scheduled call differs"
+
+
+def test_schedule_longest_first_small_grid():
+    # a few hundred rows: far fewer than 16 waves of resident workgroups -> longest first
+    torch = torch_mod()
+    t = tra()
+    wl = small_workload(800, 6, 30, 52, 128, "bf16", outer=3, tau=0.01)
+    say("schedule longest first", wl.F, wl.H, wl.W)
+    q, k, v = (t.tile_major_permute(x.to(device()), wl.F, wl.H, wl.W) for x in qkv_inputs(wl))
+    ent = torch.from_numpy(synth.entropy_like(801, wl.outer, wl.N)).to(device())
+    cnt, idx, _ = t.build_block_mask(ent, wl.F, wl.H, wl.W, wl.tau, wl.gamma)
+    order = t.sparse_schedule(cnt, wl.F, wl.H, wl.W)
+    torch.cuda.synchronize()
+    c = cnt.cpu().numpy().ravel()
+    ordv = order.cpu().numpy()
+    assert np.array_equal(np.sort(ordv), np.arange(c.size))
+    ref = np.lexsort((np.arange(c.size), -c))   # largest count first, ties by row
+    assert np.array_equal(ordv, ref)
+    _compare_scheduled(t, wl, q, k, v, cnt, idx, order)
+    # fp32 kernel and 64-query blocks take the same orders
+    wl64 = small_workload(802, 2, 9, 13, 128, "f32", bq=64, tau=0.05)
+    q, k, v = (t.tile_major_permute(x.to(device()), wl64.F, wl64.H, wl64.W) for x in qkv_inputs(wl64))
+    ent = torch.from_numpy(synth.entropy_like(803, wl64.outer, wl64.N)).to(device())
+    cnt, idx, _ = t.build_block_mask(ent, wl64.F, wl64.H, wl64.W, wl64.tau, wl64.gamma, 64)
+    order = t.sparse_schedule(cnt, wl64.F, wl64.H, wl64.W, block_q=64)
+    _compare_scheduled(t, wl64, q, k, v, cnt, idx, order)
+
+
+@pytest.mark.parametrize("wid", [3, 2])
+def test_schedule_full_size(wid):
+    # Wan2.1-14B (23,640 rows: the band order) and Wan2.1-1.3B (3,072 rows: longest first), with the
+    # GPU masks of the workload entropies; scheduled bf16 and fp8 calls equal the unscheduled ones
+    torch = torch_mod()
+    t = tra()
+    wl = workloads.get(wid)
+    say("schedule full size", wl.name)
+    q, k, v = qkv_inputs(wl)
+    qp, kp, vp = (t.tile_major_permute(x.to(device()), wl.F, wl.H, wl.W) for x in (q, k, v))
+    ent = torch.from_numpy(synth.entropy_like(810 + wid, wl.outer, wl.N)).to(device())
+    cnt, idx, _ = t.build_block_mask(ent, wl.F, wl.H, wl.W, wl.tau, wl.gamma, wl.block_q, wl.block_k)
+    order = t.sparse_schedule(cnt, wl.F, wl.H, wl.W, wl.block_q, wl.block_k)
+    torch.cuda.synchronize()
+    ordv = order.cpu().numpy()
+    total = wl.outer * wl.nqb
+    assert np.array_equal(np.sort(ordv), np.arange(total))
+    if total >= 16 * 512:
+        assert np.array_equal(ordv, _band_reference(wl.F, wl.H, wl.W, wl.block_q, wl.outer))
+    else:
+        c = cnt.cpu().numpy().ravel()
+        assert np.all(np.diff(c[ordv]) <= 0)
+    _compare_scheduled(t, wl, qp, kp, vp, cnt, idx, order)
+    q8, k8 = (t.tile_major_permute(x.to(device()).to(torch.float8_e4m3fn), wl.F, wl.H, wl.W) for x in (q, k))
+    del qp, kp
+    f1, m1 = t.block_sparse_attn_fp8(q8, k8, vp, cnt, idx, lse=True)
+    f2, m2 = t.block_sparse_attn_fp8(q8, k8, vp, cnt, idx, lse=True, order=order)
+    torch.cuda.synchronize()
+    assert torch.equal(f1.view(torch.int16), f2.view(torch.int16)) and torch.equal(m1, m2), "scheduled fp8 differs"
