@@ -12,6 +12,7 @@ Functions (names as in the C ABI, without the ``tra_`` prefix):
     dense_attn_entropy
     dense_attn_entropy_mask (the warm-up pass with the mask builder fused in)
     build_block_mask, mask_prepare, natural_prepare
+    build_block_mask_1d, mask_prepare_1d (the 1D-distance variant of the mask)
     block_sparse_attn
     block_sparse_attn_fp8 (fp8 E4M3 q and k, bf16 v and o)
     sparse_schedule, block_sparse_attn_scheduled (the order the sparse workgroups take the rows in)
@@ -26,7 +27,8 @@ import threading
 
 __all__ = [
     "TraError", "library_path", "load", "tile_major_permute", "tile_major_unpermute", "dense_attn_entropy",
-    "dense_attn_entropy_mask", "build_block_mask", "mask_prepare", "natural_prepare", "block_sparse_attn",
+    "dense_attn_entropy_mask", "build_block_mask", "mask_prepare", "natural_prepare", "build_block_mask_1d",
+    "mask_prepare_1d", "block_sparse_attn",
     "block_sparse_attn_fp8", "sparse_schedule", "block_sparse_attn_scheduled", "dense_attn_entropy_natural", "dense_attn_entropy_mask_natural", "block_sparse_attn_natural",
     "exported_symbols",
 ]
@@ -78,6 +80,8 @@ def load():
                                              P, P]
         lib.tra_mask_prepare.argtypes = [i32, i32, i32, f32, f32, i32, i32, i32, i32]
         lib.tra_natural_prepare.argtypes = [i32, i32, i32, i32, i32]
+        lib.tra_build_block_mask_1d.argtypes = [P, i32, i32, i32, i32, f32, i32, i32, i32, i32, i32, P, P, i64, P, P]
+        lib.tra_mask_prepare_1d.argtypes = [i32, i32, i32, f32, i32, i32, i32, i32]
         lib.tra_block_sparse_attn.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, f32, i32, i32, P]
         lib.tra_block_sparse_attn_fp8.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, f32, i32, i32, P]
         lib.tra_sparse_schedule.argtypes = [P, i32, i32, i32, i32, i32, i32, i32, i32, P, i64, P]
@@ -92,6 +96,7 @@ def load():
         for name in ("tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
                      "tra_build_block_mask", "tra_mask_prepare", "tra_natural_prepare", "tra_block_sparse_attn",
                      "tra_block_sparse_attn_fp8", "tra_sparse_schedule", "tra_block_sparse_attn_scheduled",
+                     "tra_build_block_mask_1d", "tra_mask_prepare_1d",
                      "tra_dense_attn_entropy_mask", "tra_dense_attn_entropy_natural",
                      "tra_block_sparse_attn_natural", "tra_dense_attn_entropy_mask_natural"):
             getattr(lib, name).restype = i32
@@ -103,7 +108,7 @@ def exported_symbols():
     return ["tra_status_string", "tra_tile_major_permute", "tra_tile_major_unpermute", "tra_dense_attn_entropy",
             "tra_build_block_mask", "tra_mask_prepare", "tra_natural_prepare", "tra_block_sparse_attn",
             "tra_block_sparse_attn_fp8", "tra_sparse_schedule", "tra_block_sparse_attn_scheduled",
-            "tra_dense_attn_entropy_mask",
+            "tra_build_block_mask_1d", "tra_mask_prepare_1d", "tra_dense_attn_entropy_mask",
             "tra_dense_attn_entropy_natural", "tra_block_sparse_attn_natural", "tra_dense_attn_entropy_mask_natural"]
 
 
@@ -292,6 +297,30 @@ def build_block_mask(entropy, F: int, H: int, W: int, tau: float, gamma: float, 
         if (want_mask or block_mask is not None) else None
     _call("tra_build_block_mask", _ptr(entropy), outer, F, H, W, float(tau), float(gamma), block_q, block_k,
           int(vote_threshold), tile_h, tile_w, _ptr(cnt), _ptr(idx), idx.numel(), _ptr(msk), _stream(entropy))
+    return cnt, idx, msk
+
+
+def mask_prepare_1d(F, H, W, tau, block_q=128, block_k=64, tile_h=8, tile_w=8) -> None:
+    _call("tra_mask_prepare_1d", F, H, W, float(tau), block_q, block_k, tile_h, tile_w)
+
+
+def build_block_mask_1d(entropy, F: int, H: int, W: int, tau: float, block_q: int = 128, block_k: int = 64,
+                        vote_threshold: int = 1, tile_h: int = 8, tile_w: int = 8, want_mask: bool = False,
+                        kv_count=None, kv_index=None, block_mask=None):
+    """The 1D-distance variant: query i keeps the keys within tau*exp(H_i)/2 of it in the natural raster
+    sequence.  entropy fp32 [outer][N] (tile-major) -> (kv_count, kv_index, mask|None) as build_block_mask."""
+    torch = _torch()
+    _dev(entropy, "entropy")
+    if entropy.dtype != torch.float32 or entropy.dim() != 2:
+        raise ValueError("entropy must be float32 [outer][N]")
+    outer, N = entropy.shape
+    nqb, nkb = -(-N // block_q), -(-N // block_k)
+    cnt = _buf(kv_count, "kv_count", (outer, nqb), torch.int32, entropy)
+    idx = _buf(kv_index, "kv_index", (outer, nqb, nkb), torch.int32, entropy)
+    msk = _buf(block_mask, "block_mask", (outer, nqb, nkb), torch.uint8, entropy) \
+        if (want_mask or block_mask is not None) else None
+    _call("tra_build_block_mask_1d", _ptr(entropy), outer, F, H, W, float(tau), block_q, block_k, int(vote_threshold),
+          tile_h, tile_w, _ptr(cnt), _ptr(idx), idx.numel(), _ptr(msk), _stream(entropy))
     return cnt, idx, msk
 
 

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtra.so")
-SOURCES = ["tra_api.cpp", "mask_sizes.cpp", "permute.hip", "mask.hip", "attention.hip", "schedule.hip"]
+SOURCES = ["tra_api.cpp", "mask_sizes.cpp", "permute.hip", "mask.hip", "attention.hip", "schedule.hip", "mask1d.hip"]
 ARCH = os.environ.get("TRA_OFFLOAD_ARCH", "gfx950")
 
 COMMON = [

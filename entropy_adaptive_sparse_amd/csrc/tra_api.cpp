@@ -124,6 +124,24 @@ void build_rects(const TileGeom &g, int bk, std::vector<int32_t> &off, std::vect
     off[(size_t)nkb] = (int32_t)rects.size();
 }
 
+// The rectangles of every k-block at a fixed stride of rmax slots (rmax = most rectangles in one
+// k-block), unused slots marked with frame -1; a used slot has w = f.
+void build_rect_slots(const TileGeom &g, int bk, std::vector<int4> &slots, int &rmax) {
+    std::vector<int32_t> off;
+    std::vector<int4> rects;
+    build_rects(g, bk, off, rects);
+    const size_t nkb = off.size() - 1;
+    rmax = 1;
+    for (size_t kb = 0; kb < nkb; ++kb) rmax = std::max(rmax, off[kb + 1] - off[kb]);
+    slots.assign(nkb * (size_t)rmax, make_int4(-1, 0, 0, -1));
+    for (size_t kb = 0; kb < nkb; ++kb)
+        for (int r = off[kb]; r < off[kb + 1]; ++r) {
+            int4 rc = rects[(size_t)r];
+            rc.w = rc.x;
+            slots[kb * (size_t)rmax + (size_t)(r - off[kb])] = rc;
+        }
+}
+
 struct TableKey {
     int dev, F, H, W, bk, th, tw;
     uint32_t tau_bits, gamma_bits;
@@ -161,32 +179,16 @@ tra_status get_tables(const TileGeom &g, float tau, float gamma, int bk, tra::Ma
         return TRA_OK;
     }
     std::vector<double> lam, lnT;
-    std::vector<int32_t> off;
-    std::vector<int4> rects;
+    std::vector<int4> slots;
+    int rmax = 1;
     const int tmax = (g.H - 1) * (g.H - 1) + (g.W - 1) * (g.W - 1);
     try {
         build_lambda(g.F, (double)tau, (double)gamma, lam);
         build_log_table(tmax, lnT);
-        build_rects(g, bk, off, rects);
+        build_rect_slots(g, bk, slots, rmax);
     } catch (const std::bad_alloc &) {
         return TRA_ERR_CAPACITY;
     }
-    // fixed stride: rmax rectangle slots per k-block, unused slots marked with frame -1
-    const size_t nkb = off.size() - 1;
-    int rmax = 1;
-    for (size_t kb = 0; kb < nkb; ++kb) rmax = std::max(rmax, off[kb + 1] - off[kb]);
-    std::vector<int4> slots;
-    try {
-        slots.assign(nkb * (size_t)rmax, make_int4(-1, 0, 0, -1));
-    } catch (const std::bad_alloc &) {
-        return TRA_ERR_CAPACITY;
-    }
-    for (size_t kb = 0; kb < nkb; ++kb)
-        for (int r = off[kb]; r < off[kb + 1]; ++r) {
-            int4 rc = rects[(size_t)r];
-            rc.w = rc.x;  // a used slot: w = f >= 0
-            slots[kb * (size_t)rmax + (size_t)(r - off[kb])] = rc;
-        }
     const size_t b_lam = align256(lam.size() * sizeof(double));
     const size_t b_lnT = align256(lnT.size() * sizeof(double));
     const size_t b_rect = align256(slots.size() * sizeof(int4));
@@ -213,6 +215,86 @@ tra_status get_tables(const TileGeom &g, float tau, float gamma, int bk, tra::Ma
     e.t.rmax = rmax;
     g_tables.emplace(key, e);
     out = e.t;
+    return TRA_OK;
+}
+
+// ------------------------------------------------------------------ 1D-distance tables
+// ln t for t < N, mu = ln tau - ln 2 (the window 2 d <= tau exp(H)), each k-block's natural-index
+// hull and its rectangles; fp64 with the C library, no contraction.
+#pragma clang fp contract(off)
+double window_mu(double tau) { return std::log(tau) - std::log(2.0); }
+#pragma clang fp contract(on)
+
+std::map<TableKey, std::pair<void *, tra::WindowTables>> g_window;
+
+tra_status get_window_tables(const TileGeom &g, float tau, int bk, tra::WindowTables &out) {
+    int dev = 0;
+    const hipError_t de = hipGetDevice(&dev);
+    if (de != hipSuccess) return from_hip(de, "hipGetDevice");
+    const TableKey key{dev, g.F, g.H, g.W, bk, g.th, g.tw, fbits(tau), 0u};
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_window.find(key);
+    if (it != g_window.end()) {
+        out = it->second.second;
+        return TRA_OK;
+    }
+    std::vector<double> lnT;
+    std::vector<int4> slots;
+    std::vector<int2> hull;
+    int rmax = 1;
+    const int nkb = (g.N + bk - 1) / bk;
+    try {
+        build_log_table(g.N - 1, lnT);
+        build_rect_slots(g, bk, slots, rmax);
+        hull.assign((size_t)nkb, make_int2(INT32_MAX, -1));
+    } catch (const std::bad_alloc &) {
+        return TRA_ERR_CAPACITY;
+    }
+    for (int kb = 0; kb < nkb; ++kb)
+        for (int r = 0; r < rmax; ++r) {
+            const int4 rc = slots[(size_t)kb * rmax + r];
+            if (rc.w < 0) continue;
+            const int y0 = rc.y & 0xffff, x0 = rc.y >> 16, y1 = rc.z & 0xffff, x1 = rc.z >> 16;
+            int2 &h = hull[(size_t)kb];
+            h.x = std::min(h.x, (rc.x * g.H + y0) * g.W + x0);
+            h.y = std::max(h.y, (rc.x * g.H + y1) * g.W + x1);
+        }
+    const size_t b_lnT = align256(lnT.size() * sizeof(double));
+    const size_t b_hull = align256(hull.size() * sizeof(int2));
+    const size_t b_rect = align256(slots.size() * sizeof(int4));
+    std::vector<char> host(b_lnT + b_hull + b_rect, 0);
+    std::memcpy(host.data(), lnT.data(), lnT.size() * sizeof(double));
+    std::memcpy(host.data() + b_lnT, hull.data(), hull.size() * sizeof(int2));
+    std::memcpy(host.data() + b_lnT + b_hull, slots.data(), slots.size() * sizeof(int4));
+    void *mem = nullptr;
+    const hipError_t me = hipMalloc(&mem, host.size());
+    if (me != hipSuccess) return from_hip(me, "hipMalloc of window tables");
+    const hipError_t ce = hipMemcpy(mem, host.data(), host.size(), hipMemcpyHostToDevice);
+    if (ce != hipSuccess) {
+        (void)hipFree(mem);
+        return from_hip(ce, "upload of window tables");
+    }
+    tra::WindowTables t{};
+    char *base = static_cast<char *>(mem);
+    t.lnT = reinterpret_cast<const double *>(base);
+    t.hull = reinterpret_cast<const int2 *>(base + b_lnT);
+    t.rects = reinterpret_cast<const int4 *>(base + b_lnT + b_hull);
+    t.lnTmax = lnT[(size_t)g.N - 1];
+    t.mu = window_mu((double)tau);
+    t.rmax = rmax;
+    g_window.emplace(key, std::make_pair(mem, t));
+    out = t;
+    return TRA_OK;
+}
+
+tra_status check_window_args(int F, int H, int W, float tau, int block_q, int block_k, int tile_h, int tile_w,
+                             TileGeom &g) {
+    const tra_status st = check_grid(F, H, W, tile_h, tile_w, g);
+    if (st != TRA_OK) return st;
+    if (!(tau > 0.0f) || !std::isfinite(tau)) return TRA_ERR_INVALID_ARG;
+    if (block_q < 1 || block_k < 1) return TRA_ERR_INVALID_ARG;
+    if ((block_q != 64 && block_q != 128) || block_k != 64) return TRA_ERR_UNSUPPORTED;
+    if (H > 32767 || W > 32767 || F > 32767) return TRA_ERR_UNSUPPORTED;  // rectangle bounds packed in 16 bits
     return TRA_OK;
 }
 
@@ -507,6 +589,37 @@ tra_status tra_mask_prepare(int F, int H, int W, float tau, float gamma, int blo
     if (st != TRA_OK) return st;
     tra::MaskTables t;
     return get_tables(g, tau, gamma, block_k, t);
+}
+
+tra_status tra_mask_prepare_1d(int F, int H, int W, float tau, int block_q, int block_k, int tile_h, int tile_w) {
+    TileGeom g;
+    const tra_status st = check_window_args(F, H, W, tau, block_q, block_k, tile_h, tile_w, g);
+    if (st != TRA_OK) return st;
+    tra::WindowTables t;
+    return get_window_tables(g, tau, block_k, t);
+}
+
+tra_status tra_build_block_mask_1d(const float *entropy, int outer, int F, int H, int W, float tau, int block_q,
+                                   int block_k, int vote_threshold, int tile_h, int tile_w, int32_t *kv_count,
+                                   int32_t *kv_index, int64_t kv_index_capacity, uint8_t *block_mask,
+                                   hipStream_t s) {
+    if (!entropy || !kv_count || !kv_index || outer < 1 || vote_threshold < 1) return TRA_ERR_INVALID_ARG;
+    TileGeom g;
+    tra_status st = check_window_args(F, H, W, tau, block_q, block_k, tile_h, tile_w, g);
+    if (st != TRA_OK) return st;
+    const int nqb = (g.N + block_q - 1) / block_q, nkb = (g.N + block_k - 1) / block_k;
+    if ((int64_t)outer * nqb > ((int64_t)1 << 31) - 1) return TRA_ERR_UNSUPPORTED;
+    if (kv_index_capacity < (int64_t)outer * nqb * nkb) return TRA_ERR_CAPACITY;
+    tra::WindowArgs a{};
+    st = get_window_tables(g, tau, block_k, a.t);
+    if (st != TRA_OK) return st;
+    a.ent = entropy;
+    a.outer = outer; a.nqb = nqb; a.nkb = nkb;
+    a.block_q = block_q; a.block_k = block_k; a.vote = vote_threshold;
+    a.g = g;
+    a.kv_count = kv_count; a.kv_index = kv_index; a.block_mask = block_mask;
+    clear_pending_error();
+    return from_hip(tra::launch_build_mask_1d(a, s), "build 1D-distance mask");
 }
 
 tra_status tra_build_block_mask(const float *entropy, int outer, int F, int H, int W, float tau, float gamma,

@@ -80,6 +80,28 @@ size_t mask_lds_bytes(int block_q, int F, int HW);
 // whether the mask state fits the four 16 KB tile buffers of the attention kernel (fused path)
 bool mask_fits_split(int block_q, int F, int HW);
 
+// 1D-distance variant: device tables for one (geometry, tau, block_k, tile) key.
+struct WindowTables {
+    const double *lnT;   // [N] ln t, lnT[0] = -inf
+    const int2 *hull;    // [nkb] smallest and largest natural index of each k-block's tokens
+    const int4 *rects;   // [nkb][rmax] k-block rectangles, as MaskTables::rects
+    double lnTmax;       // lnT[N - 1]
+    double mu;           // ln tau - ln 2
+    int rmax;
+};
+
+struct WindowArgs {
+    const float *ent;
+    int outer, nqb, nkb, block_q, block_k, vote;
+    TileGeom g;
+    WindowTables t;
+    int32_t *kv_count;
+    int32_t *kv_index;
+    uint8_t *block_mask;
+};
+
+hipError_t launch_build_mask_1d(const WindowArgs &a, hipStream_t s);
+
 // ---------------------------------------------------------------- attention
 // Block-sparse attention: the k-block a list entry e names, clamped into [0, nkb), so that any
 // list value keeps every access inside k and v.  The ragged last k-block (N % 64 != 0) is then

@@ -142,6 +142,32 @@ tra_status tra_mask_prepare(int F, int H, int W, float tau, float gamma, int blo
                             int tile_w);
 
 /*
+ * The 1D-distance variant of the mask (section 4, ablation study: the radius
+ * mask replaced by a 1D distance), in the same block-sparse format.
+ *
+ * Definition computed (bit-exact, no transcendental evaluated on the device):
+ * query i (tile-major position; natural raster index n_i = (f*H + h)*W + w)
+ * keeps key j iff d = |n_i - n_j| is 0 or
+ *      ln(d) <= (double)H_i + mu,   mu = ln tau - ln 2,
+ * with ln(d) and mu built in fp64 on the host with the C library: the budget
+ * tau * exp(H_i) of Insight I spent on a window of the flattened sequence
+ * centred on the query, 2 d <= tau * exp(H_i).  No per-frame factor (the
+ * sequence has no frame axis).  Blocks, votes, the diagonal rule and the
+ * outputs are those of tra_build_block_mask.
+ *
+ * entropy: device fp32 [outer][N], tile-major.  N = F*H*W.  tau > 0 (finite),
+ * vote_threshold >= 1, block_q in {64, 128}, block_k = 64, tile >= 1.  The
+ * first call for a geometry and tau uploads tables (ln t for t < N, the
+ * k-blocks' rectangles and natural-index bounds) synchronously
+ * (tra_mask_prepare_1d does that ahead of time).
+ */
+tra_status tra_build_block_mask_1d(const float *entropy, int outer, int F, int H, int W, float tau, int block_q,
+                                   int block_k, int vote_threshold, int tile_h, int tile_w, int32_t *kv_count,
+                                   int32_t *kv_index, int64_t kv_index_capacity, uint8_t *block_mask,
+                                   hipStream_t s);
+tra_status tra_mask_prepare_1d(int F, int H, int W, float tau, int block_q, int block_k, int tile_h, int tile_w);
+
+/*
  * Block-sparse attention over a kept mask (pipeline step 3: the regular
  * block-sparse mask runs on a block-sparse attention backend; cross-step
  * reuse: the mask from the warm-up entropies serves later denoising steps).

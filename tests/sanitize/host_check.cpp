@@ -45,6 +45,7 @@ int g_launches = 0;
 tra::MaskArgs g_mask;
 tra::AttnArgs g_attn;
 tra::ScheduleArgs g_sched;
+tra::WindowArgs g_win_args;
 }  // namespace
 
 namespace tra {
@@ -60,6 +61,11 @@ hipError_t launch_attention(const AttnArgs &a, int, int, int, bool, hipStream_t)
 
 hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t) {
     g_sched = a;
+    ++g_launches;
+    return hipSuccess;
+}
+hipError_t launch_build_mask_1d(const WindowArgs &a, hipStream_t) {
+    g_win_args = a;
     ++g_launches;
     return hipSuccess;
 }
@@ -278,7 +284,37 @@ int main() {
             prev_frame = f;
         }
     }
-    CHECK(g_launches == 11, "launch count");
+    // the 1D-distance mask: tables (ln t for t < N, k-block bounds) reach the launcher
+    {
+        const int F = 3, H = 15, W = 17, N = F * H * W, nqb = (N + 127) / 128, nkb = (N + 63) / 64;
+        std::vector<float> ent((size_t)2 * N, 4.0f);
+        std::vector<int32_t> cnt((size_t)2 * nqb), idx((size_t)2 * nqb * nkb);
+        CHECK(tra_mask_prepare_1d(F, H, W, 0.05f, 128, 64, 8, 8) == TRA_OK, "mask_prepare_1d");
+        CHECK(tra_build_block_mask_1d(ent.data(), 2, F, H, W, 0.05f, 128, 64, 1, 8, 8, cnt.data(), idx.data(),
+                                      (int64_t)idx.size(), nullptr, nullptr) == TRA_OK,
+              "build_block_mask_1d");
+        CHECK(g_win_args.nqb == nqb && g_win_args.nkb == nkb && g_win_args.t.lnTmax == std::log((double)(N - 1)),
+              "1d mask args");
+        for (int kb = 0; kb < nkb; ++kb) {
+            int lo = INT32_MAX, hi = -1;
+            tra::TileGeom g{F, H, W, 8, 8, H * W, N};
+            for (int p = kb * 64; p < std::min(N, kb * 64 + 64); ++p) {
+                lo = std::min(lo, tra::tile_major_to_natural(p, g));
+                hi = std::max(hi, tra::tile_major_to_natural(p, g));
+            }
+            CHECK(g_win_args.t.hull[kb].x == lo && g_win_args.t.hull[kb].y == hi, "k-block natural bounds");
+        }
+        CHECK(tra_build_block_mask_1d(ent.data(), 2, F, H, W, 0.0f, 128, 64, 1, 8, 8, cnt.data(), idx.data(),
+                                      (int64_t)idx.size(), nullptr, nullptr) == TRA_ERR_INVALID_ARG,
+              "1d mask, tau = 0");
+        CHECK(tra_build_block_mask_1d(ent.data(), 2, F, H, W, 0.05f, 128, 64, 1, 8, 8, cnt.data(), idx.data(),
+                                      (int64_t)idx.size() - 1, nullptr, nullptr) == TRA_ERR_CAPACITY,
+              "1d mask capacity");
+        CHECK(tra_build_block_mask_1d(ent.data(), 2, F, H, W, 0.05f, 96, 64, 1, 8, 8, cnt.data(), idx.data(),
+                                      (int64_t)idx.size(), nullptr, nullptr) == TRA_ERR_UNSUPPORTED,
+              "1d mask, block_q = 96");
+    }
+    CHECK(g_launches == 12, "launch count");
     std::printf("host sanitize ok\n");
     return 0;
 }

@@ -38,7 +38,8 @@ def test_header_declares_the_entry_points():
               "tra_build_block_mask", "tra_block_sparse_attn", "tra_mask_prepare", "tra_status_string",
               "tra_dense_attn_entropy_mask", "tra_dense_attn_entropy_natural", "tra_block_sparse_attn_natural",
               "tra_dense_attn_entropy_mask_natural", "tra_natural_prepare", "tra_block_sparse_attn_fp8",
-              "tra_sparse_schedule", "tra_block_sparse_attn_scheduled"):
+              "tra_sparse_schedule", "tra_block_sparse_attn_scheduled", "tra_build_block_mask_1d",
+              "tra_mask_prepare_1d"):
         assert n in names
 
 
@@ -245,6 +246,28 @@ def test_schedule_validation(lib):
     a = list(sb); a[6] = None; assert g(*a) == INVALID       # kv_index
     a = list(sb); a[14] = 32; assert g(*a) == UNSUPPORTED    # block_k
     a = list(sb); a[10] = 96; assert g(*a) == UNSUPPORTED    # D
+
+
+def test_mask_1d_validation(lib):
+    f = lib.tra_build_block_mask_1d
+    # ent outer F H W tau bq bk vote th tw cnt idx cap mask stream
+    base = [FAKE, 2, 4, 16, 16, 0.05, 128, 64, 1, 8, 8, FAKE2, FAKE3, 2 * 8 * 16, None, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a0=None) == INVALID              # entropy
+    assert call(a11=None) == INVALID             # kv_count
+    assert call(a1=0) == INVALID                 # outer
+    assert call(a5=0.0) == INVALID               # tau
+    assert call(a5=float("inf")) == INVALID      # tau
+    assert call(a8=0) == INVALID                 # vote threshold
+    assert call(a6=96) == UNSUPPORTED            # block_q
+    assert call(a7=32) == UNSUPPORTED            # block_k
+    assert call(a13=2 * 8 * 16 - 1) == CAPACITY  # kv_index capacity
+    assert lib.tra_mask_prepare_1d(4, 16, 16, -1.0, 128, 64, 8, 8) == INVALID
 
 
 def test_natural_prepare_validation(lib):
