@@ -5,6 +5,7 @@ resident in HBM:
     tile-major permute of q, k, v
     dense warm-up attention with fused per-query entropy (all N keys)
     entropy -> budget -> radius -> block-sparse mask
+    the order the sparse workgroups take the rows in (computed once per mask, like it)
     block-sparse attention over that mask (the reused-mask call of later steps)
     unpermute of the output
 Every stage is timed with HIP events on the stream the kernels run on.  The
@@ -31,6 +32,7 @@ METRIC = "ms/call + effective TFLOP/s (% bf16 MFMA peak), TRA block-sparse attn 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0
 
 
 def parse():
@@ -44,6 +46,9 @@ def parse():
                    help="use the oracle-calibrated tau for this retained density (0.09, 0.15, 0.19 at workload 3)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--headline-only", action="store_true",
+                   help="only the timed steps: no extra calls after them (so a profiler's per-kernel statistics cover "
+                        "the steps' kernels alone)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (3 times), to calibrate HBM counters")
     return p.parse_args()
@@ -192,6 +197,7 @@ def main():
     ent = torch.empty((wl.outer, wl.N), dtype=torch.float32, device=dev)
     cnt = torch.empty((wl.outer, wl.nqb), dtype=torch.int32, device=dev)
     idx = torch.empty((wl.outer, wl.nqb, wl.nkb), dtype=torch.int32, device=dev)
+    order = torch.empty((wl.outer * wl.nqb,), dtype=torch.int32, device=dev)
     tra.mask_prepare(wl.F, wl.H, wl.W, tau, wl.gamma, wl.block_q, wl.block_k)
     if wl.W % 4 == 0 and wl.tile_w % 4 == 0:
         tra.natural_prepare(wl.F, wl.H, wl.W, wl.tile_h, wl.tile_w)
@@ -200,7 +206,7 @@ def main():
     if wl.static_mask:
         ent_mask = torch.tensor(wl.static_entropy, dtype=torch.float32, device=dev).view(wl.outer, 1).expand(
             wl.outer, wl.N).contiguous()
-    stages = ["permute_qkv", "dense_entropy", "build_mask", "sparse_attn", "unpermute"]
+    stages = ["permute_qkv", "dense_entropy", "build_mask", "schedule", "sparse_attn", "unpermute"]
 
     def step(ev=None):
         def mark(i):
@@ -215,17 +221,19 @@ def main():
         tra.build_block_mask(ent_mask, wl.F, wl.H, wl.W, tau, wl.gamma, wl.block_q, wl.block_k, wl.vote_threshold,
                              kv_count=cnt, kv_index=idx)
         mark(3)
-        tra.block_sparse_attn(qp, kp, vp, cnt, idx, wl.block_q, wl.block_k, wl.sm_scale, out=osp)
+        tra.sparse_schedule(cnt, wl.F, wl.H, wl.W, wl.block_q, wl.block_k, wl.tile_h, wl.tile_w, out=order)
         mark(4)
-        tra.tile_major_unpermute(osp, wl.F, wl.H, wl.W, out=onat)
+        tra.block_sparse_attn_scheduled(qp, kp, vp, cnt, idx, order, wl.block_q, wl.block_k, wl.sm_scale, out=osp)
         mark(5)
+        tra.tile_major_unpermute(osp, wl.F, wl.H, wl.W, out=onat)
+        mark(6)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     print("# warmup done", file=sys.stderr, flush=True)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(args.steps):
@@ -239,83 +247,147 @@ def main():
     ms = {name: float(np.mean(v)) for name, v in per_stage.items()}
     ms_step = wall * 1e3 / args.steps
 
-    # the library's dense path without the entropy: the speed-up reference (outside the steps)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    tra.dense_attn_entropy(qp, kp, vp, wl.sm_scale, entropy=False, out=od)
-    e0.record()
-    for _ in range(2):
-        tra.dense_attn_entropy(qp, kp, vp, wl.sm_scale, entropy=False, out=od)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_dense_plain = e0.elapsed_time(e1) / 2
-    # cold variant of the sparse call: 512 MB written between calls (the last-level cache is 256 MB)
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    cold = []
-    for _ in range(3):
-        scratch.fill_(1)
-        e0.record()
-        tra.block_sparse_attn(qp, kp, vp, cnt, idx, wl.block_q, wl.block_k, wl.sm_scale, out=osp)
-        e1.record()
-        torch.cuda.synchronize()
-        cold.append(e0.elapsed_time(e1))
-    del scratch
-    ms_sparse_cold = float(np.mean(cold))
-    # the warm-up pass with the mask builder fused in (same outputs as dense_entropy + build_mask)
-    ms_fused = None
-    if wl.dtype == "bf16" and wl.D == 128 and wl.block_q == 128 and not wl.static_mask:
-        def fused():
-            tra.dense_attn_entropy_mask(qp, kp, vp, wl.F, wl.H, wl.W, tau, wl.gamma, wl.sm_scale, wl.block_q,
-                                        wl.block_k, wl.vote_threshold, out=od, ent_out=ent, kv_count=cnt,
-                                        kv_index=idx)
-        fused()
-        e0.record()
-        for _ in range(2):
-            fused()
-        e1.record()
-        torch.cuda.synchronize()
-        ms_fused = e0.elapsed_time(e1) / 2
 
-    # the permutation folded into the attention kernels (natural-order q, k, v, o; same results
-    # bit for bit): a reuse step is then one call, a warm-up one dense call plus the mask
-    ms_reuse_nat = ms_dense_nat = ms_fused_nat = None
-    if wl.dtype == "bf16" and wl.D == 128 and wl.block_q == 128 and wl.W % 4 == 0 and wl.tile_w % 4 == 0:
-        def sparse_nat():
-            tra.block_sparse_attn_natural(qd, kd, vd, cnt, idx, wl.F, wl.H, wl.W, wl.block_q, wl.block_k,
-                                          wl.sm_scale, tile_h=wl.tile_h, tile_w=wl.tile_w, out=onat)
-
-        def dense_nat():
-            tra.dense_attn_entropy_natural(qd, kd, vd, wl.F, wl.H, wl.W, wl.sm_scale, entropy=True, out=onat,
-                                           ent_out=ent, tile_h=wl.tile_h, tile_w=wl.tile_w)
-        for fn in (sparse_nat, dense_nat):
-            fn()
-        reps = max(2, args.steps)
+    def timed(fn, reps):
+        fn()
         e0.record()
         for _ in range(reps):
-            sparse_nat()
+            fn()
         e1.record()
         torch.cuda.synchronize()
-        ms_reuse_nat = e0.elapsed_time(e1) / reps
+        return e0.elapsed_time(e1) / reps
+
+    reps = max(3, args.steps)
+    ms_dense_plain = ms_reuse_b2b = ms_sparse_b2b = ms_sparse_default = ms_sparse_cold = None
+    ms_fused = ms_reuse_nat = ms_dense_nat = ms_fused_nat = None
+    if not args.headline_only:
+        # the library's dense path without the entropy: the speed-up reference (outside the steps)
+        tra.dense_attn_entropy(qp, kp, vp, wl.sm_scale, entropy=False, out=od)
         e0.record()
         for _ in range(2):
-            dense_nat()
+            tra.dense_attn_entropy(qp, kp, vp, wl.sm_scale, entropy=False, out=od)
         e1.record()
         torch.cuda.synchronize()
-        ms_dense_nat = e0.elapsed_time(e1) / 2
-        if not wl.static_mask:
-            def fused_nat():
-                tra.dense_attn_entropy_mask_natural(qd, kd, vd, wl.F, wl.H, wl.W, tau, wl.gamma, wl.sm_scale,
-                                                    wl.block_q, wl.block_k, wl.vote_threshold, wl.tile_h, wl.tile_w,
-                                                    out=onat, ent_out=ent, kv_count=cnt, kv_index=idx)
-            fused_nat()
+        ms_dense_plain = e0.elapsed_time(e1) / 2
+        # later denoising steps reuse the mask and its schedule: reuse steps back to back (permute, sparse,
+        # unpermute), the sparse call alone back to back, and the sparse call in the default order
+        def reuse_step():
+            for src, dst in ((qd, qp), (kd, kp), (vd, vp)):
+                tra.tile_major_permute(src, wl.F, wl.H, wl.W, out=dst)
+            tra.block_sparse_attn_scheduled(qp, kp, vp, cnt, idx, order, wl.block_q, wl.block_k, wl.sm_scale, out=osp)
+            tra.tile_major_unpermute(osp, wl.F, wl.H, wl.W, out=onat)
+        reps = max(3, args.steps)
+        ms_reuse_b2b = timed(reuse_step, reps)
+        ms_sparse_b2b = timed(lambda: tra.block_sparse_attn_scheduled(qp, kp, vp, cnt, idx, order, wl.block_q,
+                                                                      wl.block_k, wl.sm_scale, out=osp), reps)
+        ms_sparse_default = timed(lambda: tra.block_sparse_attn(qp, kp, vp, cnt, idx, wl.block_q, wl.block_k,
+                                                                wl.sm_scale, out=osp), reps)
+        # cold variant of the sparse call: 512 MB written between calls (the last-level cache is 256 MB)
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold = []
+        for _ in range(3):
+            scratch.fill_(1)
             e0.record()
-            for _ in range(2):
-                fused_nat()
+            tra.block_sparse_attn_scheduled(qp, kp, vp, cnt, idx, order, wl.block_q, wl.block_k, wl.sm_scale, out=osp)
             e1.record()
             torch.cuda.synchronize()
-            ms_fused_nat = e0.elapsed_time(e1) / 2
+            cold.append(e0.elapsed_time(e1))
+        del scratch
+        ms_sparse_cold = float(np.mean(cold))
+        # the warm-up pass with the mask builder fused in (same outputs as dense_entropy + build_mask)
+        ms_fused = None
+        if wl.dtype == "bf16" and wl.D == 128 and wl.block_q == 128 and not wl.static_mask:
+            def fused():
+                tra.dense_attn_entropy_mask(qp, kp, vp, wl.F, wl.H, wl.W, tau, wl.gamma, wl.sm_scale, wl.block_q,
+                                            wl.block_k, wl.vote_threshold, out=od, ent_out=ent, kv_count=cnt,
+                                            kv_index=idx)
+            fused()
+            e0.record()
+            for _ in range(2):
+                fused()
+            e1.record()
+            torch.cuda.synchronize()
+            ms_fused = e0.elapsed_time(e1) / 2
 
+        # the permutation folded into the attention kernels (natural-order q, k, v, o; same results
+        # bit for bit): a reuse step is then one call, a warm-up one dense call plus the mask
+        ms_reuse_nat = ms_dense_nat = ms_fused_nat = None
+        if wl.dtype == "bf16" and wl.D == 128 and wl.block_q == 128 and wl.W % 4 == 0 and wl.tile_w % 4 == 0:
+            def sparse_nat():
+                tra.block_sparse_attn_natural(qd, kd, vd, cnt, idx, wl.F, wl.H, wl.W, wl.block_q, wl.block_k,
+                                              wl.sm_scale, tile_h=wl.tile_h, tile_w=wl.tile_w, out=onat)
+
+            def dense_nat():
+                tra.dense_attn_entropy_natural(qd, kd, vd, wl.F, wl.H, wl.W, wl.sm_scale, entropy=True, out=onat,
+                                               ent_out=ent, tile_h=wl.tile_h, tile_w=wl.tile_w)
+            for fn in (sparse_nat, dense_nat):
+                fn()
+            reps = max(2, args.steps)
+            e0.record()
+            for _ in range(reps):
+                sparse_nat()
+            e1.record()
+            torch.cuda.synchronize()
+            ms_reuse_nat = e0.elapsed_time(e1) / reps
+            e0.record()
+            for _ in range(2):
+                dense_nat()
+            e1.record()
+            torch.cuda.synchronize()
+            ms_dense_nat = e0.elapsed_time(e1) / 2
+            if not wl.static_mask:
+                def fused_nat():
+                    tra.dense_attn_entropy_mask_natural(qd, kd, vd, wl.F, wl.H, wl.W, tau, wl.gamma, wl.sm_scale,
+                                                        wl.block_q, wl.block_k, wl.vote_threshold, wl.tile_h, wl.tile_w,
+                                                        out=onat, ent_out=ent, kv_count=cnt, kv_index=idx)
+                fused_nat()
+                e0.record()
+                for _ in range(2):
+                    fused_nat()
+                e1.record()
+                torch.cuda.synchronize()
+                ms_fused_nat = e0.elapsed_time(e1) / 2
     pairs = retained_pairs(torch, cnt, idx, wl.N, wl.block_q, wl.block_k)
     density = pairs / (wl.outer * float(wl.N) ** 2)
+
+    # fp8 queries and keys (OCP E4M3, rounded once from the bf16 values, outside the timing) with bf16
+    # values: the sparse call over the same mask and schedule
+    fp8 = None
+    if wl.dtype == "bf16" and wl.D == 128 and wl.block_q == 128 and not args.headline_only:
+        q8 = qp.to(torch.float8_e4m3fn)
+        k8 = kp.to(torch.float8_e4m3fn)
+        ms_fp8 = timed(lambda: tra.block_sparse_attn_fp8(q8, k8, vp, cnt, idx, wl.block_q, wl.block_k, wl.sm_scale,
+                                                         out=osp, order=order), reps)
+        del q8, k8
+        tf8 = 4.0 * wl.D * pairs / (ms_fp8 * 1e-3) / 1e12
+        # half the work (q.k) at the fp8 rate, half (p.v) at the bf16 rate
+        blended = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
+        fp8 = {"ms": round(ms_fp8, 4), "achieved": round(tf8, 2), "unit": "TFLOP/s", "peak_blended": round(blended, 1),
+               "frac_blended": round(tf8 / blended, 4), "frac_bf16_peak": round(tf8 / PEAK_BF16_TFLOPS, 4),
+               "speedup_vs_bf16": round(ms_sparse_b2b / ms_fp8, 3),
+               "note": "q, k fp8 E4M3 (scores on the fp8 matrix cores), v, o bf16; same mask and schedule; "
+                       "back to back, as the bf16 ms_sparse_back_to_back"}
+
+    # the 1D-distance variant of the mask (the ablation of the radius mask), from the same warm-up
+    # entropies and tau, and the sparse call over its lists
+    mask1d = None
+    if not wl.static_mask and not args.headline_only:
+        cnt1 = torch.empty_like(cnt)
+        idx1 = torch.empty_like(idx)
+        tra.mask_prepare_1d(wl.F, wl.H, wl.W, tau, wl.block_q, wl.block_k, wl.tile_h, wl.tile_w)
+        ms_m1 = timed(lambda: tra.build_block_mask_1d(ent, wl.F, wl.H, wl.W, tau, wl.block_q, wl.block_k,
+                                                      wl.vote_threshold, wl.tile_h, wl.tile_w, kv_count=cnt1,
+                                                      kv_index=idx1), reps)
+        order1 = tra.sparse_schedule(cnt1, wl.F, wl.H, wl.W, wl.block_q, wl.block_k, wl.tile_h, wl.tile_w)
+        ms_s1 = timed(lambda: tra.block_sparse_attn_scheduled(qp, kp, vp, cnt1, idx1, order1, wl.block_q, wl.block_k,
+                                                              wl.sm_scale, out=osp), reps)
+        pairs1 = retained_pairs(torch, cnt1, idx1, wl.N, wl.block_q, wl.block_k)
+        mask1d = {"ms_mask": round(ms_m1, 4), "density": round(pairs1 / (wl.outer * float(wl.N) ** 2), 5),
+                  "ms_sparse": round(ms_s1, 4),
+                  "sparse_tflops": round(4.0 * wl.D * pairs1 / (ms_s1 * 1e-3) / 1e12, 2),
+                  "note": "same tau and entropies as the disk mask; sparse call back to back with its own schedule"}
+        del cnt1, idx1, order1
     sparse_flops = 4.0 * wl.D * pairs
     dense_flops = wl.dense_flops
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -328,6 +400,9 @@ def main():
     nnz = int(cnt.to(torch.int64).sum().item())
     mask_bytes = 4 * wl.outer * wl.N + 4 * nnz + 4 * wl.outer * wl.nqb
     mask_gbs = mask_bytes / (ms["build_mask"] * 1e-3) / 1e9
+
+    def r4(x):
+        return None if x is None else round(x, 4)
 
     result = {
         "metric": METRIC,
@@ -349,11 +424,14 @@ def main():
             "retained_density": round(density, 5), "static_mask": wl.static_mask,
         },
         "ms_per_call": {k2: round(v2, 4) for k2, v2 in ms.items()},
-        "ms_dense_no_entropy": round(ms_dense_plain, 4),
-        "ms_sparse_cold": round(ms_sparse_cold, 4),
+        "ms_dense_no_entropy": r4(ms_dense_plain),
+        "ms_sparse_cold": r4(ms_sparse_cold),
         "ms_warmup_separate": round(ms["dense_entropy"] + ms["build_mask"], 4),
         "ms_warmup_fused": None if ms_fused is None else round(ms_fused, 4),
         "ms_reuse_step": round(ms["permute_qkv"] + ms["sparse_attn"] + ms["unpermute"], 4),
+        "ms_reuse_step_back_to_back": r4(ms_reuse_b2b),
+        "ms_sparse_back_to_back": r4(ms_sparse_b2b),
+        "ms_sparse_default_order": r4(ms_sparse_default),
         "ms_reuse_step_natural": None if ms_reuse_nat is None else round(ms_reuse_nat, 4),
         "ms_dense_entropy_natural": None if ms_dense_nat is None else round(ms_dense_nat, 4),
         "ms_warmup_fused_natural": None if ms_fused_nat is None else round(ms_fused_nat, 4),
@@ -375,7 +453,9 @@ def main():
             "build_mask": {"bound": "alu", "achieved_hbm": round(mask_gbs, 2), "unit": "GB/s", "bytes": mask_bytes,
                            "pct_of_sparse_time": round(100.0 * ms["build_mask"] / ms["sparse_attn"], 2)},
         },
-        "speedup_sparse_vs_dense": round(ms_dense_plain / ms["sparse_attn"], 3),
+        "fp8_sparse": fp8,
+        "mask_1d": mask1d,
+        "speedup_sparse_vs_dense": None if ms_dense_plain is None else round(ms_dense_plain / ms["sparse_attn"], 3),
         "speedup_target": round(0.6 / density, 3) if density > 0 else None,
     }
 

@@ -70,11 +70,18 @@ __device__ inline int xcd_remap(int bid, int total) {
 }
 
 // The (head, q-block) row workgroup b runs: order[b] when the caller passes a schedule (clamped,
-// so any value stays in bounds), else the XCD order above.
+// so any value stays in bounds); else, with one head's band order, that order dealt to the XCDs in
+// runs (the schedule's band order, computed here); else the XCD order above.
 __device__ inline int row_of_workgroup(const AttnArgs &a, int b, int total) {
+    typedef const int32_t __attribute__((address_space(4))) *cint_t;
     if (a.order) {
-        const int r = ((const int32_t __attribute__((address_space(4))) *)a.order)[b];
+        const int r = ((cint_t)a.order)[b];
         return min(max(r, 0), total - 1);
+    }
+    if (a.band) {
+        const int L = xcd_runs(b, total);
+        const int o = L / a.nqb;
+        return o * a.nqb + ((cint_t)a.band)[L - o * a.nqb];
     }
     return xcd_remap(b, total);
 }

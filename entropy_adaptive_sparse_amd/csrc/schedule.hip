@@ -18,15 +18,6 @@ namespace tra {
 
 namespace {
 
-// workgroup b -> position in the run order: XCD x = b mod 8 takes runs of kBandRun consecutive
-// positions; the ragged last row of runs keeps the identity (every position once)
-__device__ inline int xcd_runs(int b, int total) {
-    const int full = (total / (8 * kBandRun)) * (8 * kBandRun);
-    if (b >= full) return b;
-    const int x = b & 7, k = b >> 3;
-    return (k / kBandRun) * (8 * kBandRun) + x * kBandRun + (k % kBandRun);
-}
-
 __global__ void band_order_kernel(const int32_t *__restrict__ band, int nqb, int total, int32_t *__restrict__ order) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= total) return;

@@ -705,6 +705,9 @@ tra_status tra_block_sparse_attn_natural(const void *q, const void *k, const voi
     a.kv_count = kv_count; a.kv_index = kv_index;
     st = get_nat_table(g, a.nat4);
     if (st != TRA_OK) return st;
+    // the geometry is known here: the workgroups take the rows in the spatial band order
+    st = get_band_table(g, block_q, a.band);
+    if (st != TRA_OK) return st;
     clear_pending_error();
     return from_hip(tra::launch_attention_natural(a, true, s), "sparse attention (natural order)");
 }

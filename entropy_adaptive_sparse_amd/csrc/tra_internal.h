@@ -127,6 +127,9 @@ struct AttnArgs {
     // null: workgroups take the rows in the library's default order; otherwise workgroup b runs row
     // order[b] (clamped into [0, outer * nqb)), the order tra_sparse_schedule writes
     const int32_t *order;
+    // without an order: null, or one head's q-blocks in the spatial band order (nqb entries), dealt to
+    // the XCDs in runs as tra_sparse_schedule's band order
+    const int32_t *band;
     int outer, N, nqb, nkb;
     float c;          // sm_scale * log2(e)
     float sm_scale;
@@ -142,6 +145,16 @@ hipError_t launch_attention(const AttnArgs &a, int D, int dtype, int block_q, bo
 // ---------------------------------------------------------------- schedule
 // Rows per run of the spatial band order on one XCD (about the workgroups an XCD holds at once).
 constexpr int kBandRun = 64;
+
+// workgroup b -> position in the run order: XCD x = b mod 8 takes runs of kBandRun consecutive
+// positions, the runs of the 8 XCDs advancing together; the ragged last row of runs keeps the
+// identity (every position once)
+__device__ inline int xcd_runs(int b, int total) {
+    const int full = (total / (8 * kBandRun)) * (8 * kBandRun);
+    if (b >= full) return b;
+    const int x = b & 7, k = b >> 3;
+    return (k / kBandRun) * (8 * kBandRun) + x * kBandRun + (k % kBandRun);
+}
 
 struct ScheduleArgs {
     const int32_t *kv_count;  // [outer][nqb] (longest-first order)

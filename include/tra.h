@@ -288,7 +288,10 @@ tra_status tra_dense_attn_entropy_mask(const void *q, const void *k, const void 
  * tra_build_block_mask reads, and kv_count / kv_index are the tile-major
  * block lists tra_build_block_mask writes.
  *
- * q, k, v, o: device, [outer][N][128] bf16, natural order, N = F*H*W.
+ * q, k, v, o: device, [outer][N][128] bf16, natural order, N = F*H*W.  The
+ * sparse call takes its rows in the spatial band order of tra_sparse_schedule
+ * (the geometry is known here; the first call for a geometry uploads that
+ * table too).
  * Supported: bf16, D = 128, W and tile_w multiples of 4 (then every aligned
  * group of four tile-major positions is a run of four natural rows), N*D*2 <
  * 2^32; sparse: block_q = 128, block_k = 64.  Anything else returns

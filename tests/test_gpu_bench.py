@@ -1,6 +1,6 @@
 """GPU: bench.py keeps its one-line JSON contract (metric, value, roofline with the sparse
-kernel's traffic, null unless the committed counter summary matches the kernel source) on a
-short run."""
+kernel's HBM traffic from the committed counter summary of the present kernel source) on a
+short run, with the fp8 and 1D-distance rows."""
 import json
 import os
 import subprocess
@@ -28,8 +28,14 @@ def test_bench_json_line():
     assert d["unit"] == "TFLOP/s" and d["dtype"] == "bf16" and d["value"] > 0
     rf = d["roofline"]
     assert rf["bound"] == "mfma" and rf["peak"] == 2500.0 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
-    # null while the committed counter summary was taken on another kernel source (the CPU
-    # suite checks that it is current)
-    assert rf["traffic"] is None or (isinstance(rf["traffic"], int) and rf["traffic"] > 3.0e9)
+    # the counter summary under profiles/ was taken on this kernel source: traffic is live (at least
+    # q, k, v and o once)
+    assert isinstance(rf["traffic"], int) and rf["traffic"] > 3.0e9
     assert d["config"]["workload"] == "wan2.1-14b-720p-21x45x80"
     assert all(v > 0 for v in d["ms_per_call"].values())
+    assert set(d["ms_per_call"]) == {"permute_qkv", "dense_entropy", "build_mask", "schedule", "sparse_attn",
+                                     "unpermute"}
+    f8 = d["fp8_sparse"]
+    assert f8["ms"] > 0 and abs(f8["frac_blended"] - f8["achieved"] / f8["peak_blended"]) < 1e-3
+    m1 = d["mask_1d"]
+    assert m1["ms_mask"] > 0 and 0.0 < m1["density"] <= 1.0 and m1["ms_sparse"] > 0
