@@ -167,6 +167,19 @@ uint32_t fbits(float v) {
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
+// Inserts an uploaded table into its cache; on failure (std::bad_alloc from the map) frees the
+// device copy, so no exception leaves the library and nothing leaks.
+template <class Map, class Key, class Val>
+tra_status cache_insert(Map &m, const Key &key, const Val &val, void *mem) {
+    try {
+        m.emplace(key, val);
+    } catch (const std::bad_alloc &) {
+        (void)hipFree(mem);
+        return TRA_ERR_CAPACITY;
+    }
+    return TRA_OK;
+}
+
 tra_status get_tables(const TileGeom &g, float tau, float gamma, int bk, tra::MaskTables &out) {
     int dev = 0;
     const hipError_t de = hipGetDevice(&dev);
@@ -180,19 +193,21 @@ tra_status get_tables(const TileGeom &g, float tau, float gamma, int bk, tra::Ma
     }
     std::vector<double> lam, lnT;
     std::vector<int4> slots;
+    std::vector<char> host;
     int rmax = 1;
     const int tmax = (g.H - 1) * (g.H - 1) + (g.W - 1) * (g.W - 1);
+    size_t b_lam = 0, b_lnT = 0, b_rect = 0;
     try {
         build_lambda(g.F, (double)tau, (double)gamma, lam);
         build_log_table(tmax, lnT);
         build_rect_slots(g, bk, slots, rmax);
+        b_lam = align256(lam.size() * sizeof(double));
+        b_lnT = align256(lnT.size() * sizeof(double));
+        b_rect = align256(slots.size() * sizeof(int4));
+        host.assign(b_lam + b_lnT + b_rect, 0);
     } catch (const std::bad_alloc &) {
         return TRA_ERR_CAPACITY;
     }
-    const size_t b_lam = align256(lam.size() * sizeof(double));
-    const size_t b_lnT = align256(lnT.size() * sizeof(double));
-    const size_t b_rect = align256(slots.size() * sizeof(int4));
-    std::vector<char> host(b_lam + b_lnT + b_rect, 0);
     std::memcpy(host.data(), lam.data(), lam.size() * sizeof(double));
     std::memcpy(host.data() + b_lam, lnT.data(), lnT.size() * sizeof(double));
     std::memcpy(host.data() + b_lam + b_lnT, slots.data(), slots.size() * sizeof(int4));
@@ -213,7 +228,8 @@ tra_status get_tables(const TileGeom &g, float tau, float gamma, int bk, tra::Ma
     e.t.tmax = tmax;
     e.t.lnTmax = lnT[(size_t)tmax];
     e.t.rmax = rmax;
-    g_tables.emplace(key, e);
+    const tra_status ins = cache_insert(g_tables, key, e, mem);
+    if (ins != TRA_OK) return ins;
     out = e.t;
     return TRA_OK;
 }
@@ -241,6 +257,7 @@ tra_status get_window_tables(const TileGeom &g, float tau, int bk, tra::WindowTa
     std::vector<double> lnT;
     std::vector<int4> slots;
     std::vector<int2> hull;
+    std::vector<char> host;
     int rmax = 1;
     const int nkb = (g.N + bk - 1) / bk;
     try {
@@ -262,7 +279,11 @@ tra_status get_window_tables(const TileGeom &g, float tau, int bk, tra::WindowTa
     const size_t b_lnT = align256(lnT.size() * sizeof(double));
     const size_t b_hull = align256(hull.size() * sizeof(int2));
     const size_t b_rect = align256(slots.size() * sizeof(int4));
-    std::vector<char> host(b_lnT + b_hull + b_rect, 0);
+    try {
+        host.assign(b_lnT + b_hull + b_rect, 0);
+    } catch (const std::bad_alloc &) {
+        return TRA_ERR_CAPACITY;
+    }
     std::memcpy(host.data(), lnT.data(), lnT.size() * sizeof(double));
     std::memcpy(host.data() + b_lnT, hull.data(), hull.size() * sizeof(int2));
     std::memcpy(host.data() + b_lnT + b_hull, slots.data(), slots.size() * sizeof(int4));
@@ -282,7 +303,8 @@ tra_status get_window_tables(const TileGeom &g, float tau, int bk, tra::WindowTa
     t.lnTmax = lnT[(size_t)g.N - 1];
     t.mu = window_mu((double)tau);
     t.rmax = rmax;
-    g_window.emplace(key, std::make_pair(mem, t));
+    const tra_status ins = cache_insert(g_window, key, std::make_pair(mem, t), mem);
+    if (ins != TRA_OK) return ins;
     out = t;
     return TRA_OK;
 }
@@ -344,7 +366,8 @@ tra_status get_nat_table(const TileGeom &g, const int32_t *&out) {
         (void)hipFree(mem);
         return from_hip(ce, "upload of the natural-order map");
     }
-    g_nat.emplace(key, mem);
+    const tra_status ins = cache_insert(g_nat, key, mem, mem);
+    if (ins != TRA_OK) return ins;
     out = static_cast<const int32_t *>(mem);
     return TRA_OK;
 }
@@ -397,7 +420,8 @@ tra_status get_band_table(const TileGeom &g, int bq, const int32_t *&out) {
         (void)hipFree(mem);
         return from_hip(ce, "upload of the band order");
     }
-    g_band.emplace(key, mem);
+    const tra_status ins = cache_insert(g_band, key, mem, mem);
+    if (ins != TRA_OK) return ins;
     out = static_cast<const int32_t *>(mem);
     return TRA_OK;
 }
@@ -412,7 +436,13 @@ tra_status compute_units(int &cus) {
         int n = 0;
         e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return from_hip(e, "hipDeviceGetAttribute");
-        it = g_cus.emplace(dev, std::max(1, n)).first;
+        cus = std::max(1, n);
+        try {
+            g_cus.emplace(dev, cus);
+        } catch (const std::bad_alloc &) {
+            // not cached; the count is still right for this call
+        }
+        return TRA_OK;
     }
     cus = it->second;
     return TRA_OK;
