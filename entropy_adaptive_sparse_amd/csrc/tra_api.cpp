@@ -454,6 +454,16 @@ constexpr int kLptWaves = 16;
 // Largest nkb the longest-first sort holds in its LDS histogram.
 constexpr int kLptMaxBins = 16383;
 
+// What tra_sparse_schedule looks up for this geometry and block_q: the band table and the
+// device's compute-unit count, built ahead of a timed region or a stream capture.
+tra_status prepare_schedule(const TileGeom &g, int block_q) {
+    int cus = 0;
+    const tra_status st = compute_units(cus);
+    if (st != TRA_OK) return st;
+    const int32_t *band = nullptr;
+    return get_band_table(g, block_q, band);
+}
+
 // Checks shared by the natural-order attention entry points (after check_attn_common).
 tra_status check_natural(int F, int H, int W, int D, tra_dtype dt, int tile_h, int tile_w, TileGeom &g) {
     const tra_status st = check_grid(F, H, W, tile_h, tile_w, g);
@@ -615,18 +625,22 @@ tra_status tra_dense_attn_entropy(const void *q, const void *k, const void *v, v
 tra_status tra_mask_prepare(int F, int H, int W, float tau, float gamma, int block_q, int block_k, int tile_h,
                             int tile_w) {
     TileGeom g;
-    const tra_status st = check_mask_args(F, H, W, tau, gamma, block_q, block_k, tile_h, tile_w, g);
+    tra_status st = check_mask_args(F, H, W, tau, gamma, block_q, block_k, tile_h, tile_w, g);
     if (st != TRA_OK) return st;
     tra::MaskTables t;
-    return get_tables(g, tau, gamma, block_k, t);
+    st = get_tables(g, tau, gamma, block_k, t);
+    if (st != TRA_OK) return st;
+    return prepare_schedule(g, block_q);
 }
 
 tra_status tra_mask_prepare_1d(int F, int H, int W, float tau, int block_q, int block_k, int tile_h, int tile_w) {
     TileGeom g;
-    const tra_status st = check_window_args(F, H, W, tau, block_q, block_k, tile_h, tile_w, g);
+    tra_status st = check_window_args(F, H, W, tau, block_q, block_k, tile_h, tile_w, g);
     if (st != TRA_OK) return st;
     tra::WindowTables t;
-    return get_window_tables(g, tau, block_k, t);
+    st = get_window_tables(g, tau, block_k, t);
+    if (st != TRA_OK) return st;
+    return prepare_schedule(g, block_q);
 }
 
 tra_status tra_build_block_mask_1d(const float *entropy, int outer, int F, int H, int W, float tau, int block_q,
@@ -692,10 +706,13 @@ tra_status tra_dense_attn_entropy_mask_natural(const void *q, const void *k, con
 
 tra_status tra_natural_prepare(int F, int H, int W, int tile_h, int tile_w) {
     TileGeom g;
-    const tra_status st = check_natural(F, H, W, 128, TRA_BF16, tile_h, tile_w, g);
+    tra_status st = check_natural(F, H, W, 128, TRA_BF16, tile_h, tile_w, g);
     if (st != TRA_OK) return st;
     const int32_t *map = nullptr;
-    return get_nat_table(g, map);
+    st = get_nat_table(g, map);
+    if (st != TRA_OK) return st;
+    const int32_t *band = nullptr;  // the natural sparse call's row order (block_q = 128)
+    return get_band_table(g, 128, band);
 }
 
 tra_status tra_dense_attn_entropy_natural(const void *q, const void *k, const void *v, void *o, float *entropy,

@@ -26,11 +26,14 @@
  *    nothing.  A failing HIP call returns TRA_ERR_HIP.  No C++ exception
  *    crosses the ABI.
  *  - Library state: a per-device cache of small fp64 tables and block
- *    geometry for tra_build_block_mask, and of the tile-major map for the
- *    natural-order attention calls, guarded by a mutex.  Its first use for a
- *    geometry allocates and uploads them synchronously (tra_mask_prepare and
- *    tra_natural_prepare do that ahead of time); entries live until the
- *    process ends.
+ *    geometry for the mask builders, of the band order for the schedule, and
+ *    of the tile-major map for the natural-order attention calls, guarded by a
+ *    mutex.  Its first use for a geometry allocates and uploads them
+ *    synchronously.  tra_mask_prepare, tra_mask_prepare_1d and
+ *    tra_natural_prepare do that ahead of time: afterwards the calls for that
+ *    geometry neither allocate nor copy between host and device, so they can
+ *    run inside a timed region or be recorded into a HIP graph by stream
+ *    capture.  Entries live until the process ends.
  */
 #ifndef TRA_H_
 #define TRA_H_
@@ -136,8 +139,10 @@ tra_status tra_build_block_mask(const float *entropy, int outer, int F, int H, i
                                 int32_t *kv_count, int32_t *kv_index, int64_t kv_index_capacity,
                                 uint8_t *block_mask, hipStream_t s);
 
-/* Builds and uploads the tables tra_build_block_mask needs for this geometry
- * on the current device (blocking), so that a timed call does no upload. */
+/* Builds and uploads, on the current device (blocking), the tables that
+ * tra_build_block_mask and tra_dense_attn_entropy_mask need for this geometry,
+ * and the band table and compute-unit count that tra_sparse_schedule needs for
+ * it and block_q, so that those calls do no allocation or upload later. */
 tra_status tra_mask_prepare(int F, int H, int W, float tau, float gamma, int block_q, int block_k, int tile_h,
                             int tile_w);
 
@@ -165,6 +170,9 @@ tra_status tra_build_block_mask_1d(const float *entropy, int outer, int F, int H
                                    int block_k, int vote_threshold, int tile_h, int tile_w, int32_t *kv_count,
                                    int32_t *kv_index, int64_t kv_index_capacity, uint8_t *block_mask,
                                    hipStream_t s);
+/* Builds and uploads, on the current device (blocking), the tables of tra_build_block_mask_1d for
+ * this geometry and tau, and the band table and compute-unit count of tra_sparse_schedule for it
+ * and block_q.  Arguments and errors as tra_build_block_mask_1d's. */
 tra_status tra_mask_prepare_1d(int F, int H, int W, float tau, int block_q, int block_k, int tile_h, int tile_w);
 
 /*
@@ -231,7 +239,8 @@ tra_status tra_block_sparse_attn_fp8(const void *q, const void *k, const void *v
  * order); order: device int32, order_capacity elements (fewer than
  * outer * nqb returns TRA_ERR_CAPACITY).  block_q in {64, 128}, block_k = 64.
  * The first call for a geometry builds and uploads the band table
- * (nqb int32) synchronously; it stays in the per-device cache.
+ * (nqb int32) synchronously; it stays in the per-device cache
+ * (tra_mask_prepare and tra_mask_prepare_1d do that ahead of time).
  */
 tra_status tra_sparse_schedule(const int32_t *kv_count, int outer, int F, int H, int W, int block_q, int block_k,
                                int tile_h, int tile_w, int32_t *order, int64_t order_capacity, hipStream_t s);
@@ -312,8 +321,9 @@ tra_status tra_dense_attn_entropy_mask_natural(const void *q, const void *k, con
                                                int vote_threshold, int tile_h, int tile_w, int32_t *kv_count,
                                                int32_t *kv_index, int64_t kv_index_capacity, uint8_t *block_mask,
                                                hipStream_t s);
-/* Builds and uploads the tile-major map the natural-order calls use for this geometry on the
- * current device (blocking), so that a timed call does no allocation or upload.  Returns
+/* Builds and uploads the tile-major map and the band order (block_q = 128) the natural-order
+ * calls use for this geometry on the current device (blocking), so that a timed or captured
+ * call does no allocation or upload.  Returns
  * TRA_ERR_UNSUPPORTED for the geometries those calls reject (W or tile_w not a multiple of 4),
  * TRA_ERR_INVALID_ARG for non-positive sizes. */
 tra_status tra_natural_prepare(int F, int H, int W, int tile_h, int tile_w);

@@ -15,12 +15,17 @@ using std::min;
 #include <vector>
 
 // ---------------------------------------------------------------- stand-ins
+// allocations, host <-> device copies and attribute queries the library makes (none may follow
+// the prepare calls on the paths they prepare)
+int g_mallocs = 0, g_copies = 0, g_attrs = 0;
+
 extern "C" {
 hipError_t hipGetDevice(int *d) {
     *d = 0;
     return hipSuccess;
 }
 hipError_t hipMalloc(void **p, size_t n) {
+    ++g_mallocs;
     *p = std::malloc(n);
     return *p ? hipSuccess : hipErrorOutOfMemory;
 }
@@ -29,11 +34,13 @@ hipError_t hipFree(void *p) {
     return hipSuccess;
 }
 hipError_t hipMemcpy(void *dst, const void *src, size_t n, hipMemcpyKind) {
+    ++g_copies;
     std::memcpy(dst, src, n);
     return hipSuccess;
 }
 hipError_t hipGetLastError(void) { return hipSuccess; }
 hipError_t hipDeviceGetAttribute(int *v, hipDeviceAttribute_t, int) {
+    ++g_attrs;
     *v = 256;
     return hipSuccess;
 }
@@ -314,7 +321,53 @@ int main() {
                                       (int64_t)idx.size(), nullptr, nullptr) == TRA_ERR_UNSUPPORTED,
               "1d mask, block_q = 96");
     }
-    CHECK(g_launches == 12, "launch count");
+    // after the prepare calls, every call of the step for that geometry allocates, copies and
+    // queries nothing (so a caller may record the step into a HIP graph by stream capture)
+    {
+        const int F = 5, H = 24, W = 40, N = F * H * W, D = 128, nqb = (N + 127) / 128, nkb = (N + 63) / 64;
+        const float tau = 0.04f, gamma = 0.5f, sc = 0.088f;
+        CHECK(tra_mask_prepare(F, H, W, tau, gamma, 128, 64, 8, 8) == TRA_OK, "prepare (step)");
+        CHECK(tra_mask_prepare_1d(F, H, W, tau, 128, 64, 8, 8) == TRA_OK, "prepare 1d (step)");
+        CHECK(tra_natural_prepare(F, H, W, 8, 8) == TRA_OK, "natural prepare (step)");
+        const int m0 = g_mallocs, c0 = g_copies, a0 = g_attrs, l0 = g_launches;
+        std::vector<uint16_t> q((size_t)2 * N * D), k(q.size()), v(q.size()), t(q.size()), o(q.size());
+        std::vector<float> ent((size_t)2 * N, 6.0f), lse((size_t)2 * N);
+        std::vector<int32_t> cnt((size_t)2 * nqb, 3), idx((size_t)2 * nqb * nkb, 0), order((size_t)2 * nqb);
+        const int outer_band = 256;  // 256 x 38 rows: past 16 waves of 2 x 256 workgroups, the band order
+        std::vector<int32_t> cnt_band((size_t)outer_band * nqb, 3), order_band((size_t)outer_band * nqb);
+        CHECK(tra_tile_major_permute(q.data(), t.data(), 2, F, H, W, D, TRA_BF16, 8, 8, nullptr) == TRA_OK, "step permute");
+        CHECK(tra_dense_attn_entropy(t.data(), k.data(), v.data(), o.data(), ent.data(), lse.data(), 2, N, D, TRA_BF16,
+                                     sc, nullptr) == TRA_OK, "step dense");
+        CHECK(tra_build_block_mask(ent.data(), 2, F, H, W, tau, gamma, 128, 64, 1, 8, 8, cnt.data(), idx.data(),
+                                   (int64_t)idx.size(), nullptr, nullptr) == TRA_OK, "step mask");
+        CHECK(tra_build_block_mask_1d(ent.data(), 2, F, H, W, tau, 128, 64, 1, 8, 8, cnt.data(), idx.data(),
+                                      (int64_t)idx.size(), nullptr, nullptr) == TRA_OK, "step 1d mask");
+        CHECK(tra_sparse_schedule(cnt.data(), 2, F, H, W, 128, 64, 8, 8, order.data(), (int64_t)order.size(),
+                                  nullptr) == TRA_OK && g_sched.lpt, "step schedule (longest first)");
+        CHECK(tra_sparse_schedule(cnt_band.data(), outer_band, F, H, W, 128, 64, 8, 8, order_band.data(),
+                                  (int64_t)order_band.size(), nullptr) == TRA_OK && !g_sched.lpt,
+              "step schedule (band)");
+        CHECK(tra_block_sparse_attn_scheduled(t.data(), k.data(), v.data(), o.data(), lse.data(), cnt.data(),
+                                              idx.data(), order.data(), 2, N, D, TRA_BF16, sc, 128, 64,
+                                              nullptr) == TRA_OK, "step scheduled sparse");
+        CHECK(tra_tile_major_unpermute(o.data(), t.data(), 2, F, H, W, D, TRA_BF16, 8, 8, nullptr) == TRA_OK,
+              "step unpermute");
+        CHECK(tra_dense_attn_entropy_mask(t.data(), k.data(), v.data(), o.data(), ent.data(), nullptr, 2, F, H, W, D,
+                                          TRA_BF16, sc, tau, gamma, 128, 64, 1, 8, 8, cnt.data(), idx.data(),
+                                          (int64_t)idx.size(), nullptr, nullptr) == TRA_OK, "step fused");
+        CHECK(tra_dense_attn_entropy_natural(q.data(), k.data(), v.data(), o.data(), ent.data(), nullptr, 2, F, H, W,
+                                             D, TRA_BF16, sc, 8, 8, nullptr) == TRA_OK, "step natural dense");
+        CHECK(tra_dense_attn_entropy_mask_natural(q.data(), k.data(), v.data(), o.data(), ent.data(), nullptr, 2, F, H,
+                                                  W, D, TRA_BF16, sc, tau, gamma, 128, 64, 1, 8, 8, cnt.data(),
+                                                  idx.data(), (int64_t)idx.size(), nullptr, nullptr) == TRA_OK,
+              "step natural fused");
+        CHECK(tra_block_sparse_attn_natural(q.data(), k.data(), v.data(), o.data(), nullptr, cnt.data(), idx.data(), 2,
+                                            F, H, W, D, TRA_BF16, sc, 128, 64, 8, 8, nullptr) == TRA_OK &&
+                  g_attn.band != nullptr, "step natural sparse");
+        CHECK(g_launches - l0 == 12, "step launches");
+        CHECK(g_mallocs == m0 && g_copies == c0 && g_attrs == a0, "no allocation, copy or query after prepare");
+    }
+    CHECK(g_launches == 24, "launch count");
     std::printf("host sanitize ok\n");
     return 0;
 }
