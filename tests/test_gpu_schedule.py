@@ -108,3 +108,45 @@ def test_schedule_full_size(wid):
     f2, m2 = t.block_sparse_attn_fp8(q8, k8, vp, cnt, idx, lse=True, order=order)
     torch.cuda.synchronize()
     assert torch.equal(f1.view(torch.int16), f2.view(torch.int16)) and torch.equal(m1, m2), "scheduled fp8 differs"
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_scheduled_out_of_contract_order(kind):
+    # order entries outside [0, rows) are clamped into that range and a duplicated row runs twice:
+    # every access stays inside the buffers, each row some entry names (after clamping) equals the
+    # unscheduled call bit for bit, and rows no entry names keep what the output held before
+    torch = torch_mod()
+    t = tra()
+    wl = small_workload(820, 3, 15, 20, 128, "bf16", outer=2, tau=0.05)
+    say("out-of-contract order", kind, wl.F, wl.H, wl.W)
+    q, k, v = (t.tile_major_permute(x.to(device()), wl.F, wl.H, wl.W) for x in qkv_inputs(wl))
+    if kind == "fp8":
+        q, k = q.to(torch.float8_e4m3fn), k.to(torch.float8_e4m3fn)
+    ent = torch.from_numpy(synth.entropy_like(821, wl.outer, wl.N)).to(device())
+    cnt, idx, _ = t.build_block_mask(ent, wl.F, wl.H, wl.W, wl.tau, wl.gamma)
+    total = wl.outer * wl.nqb
+    ordv = np.arange(total, dtype=np.int32)
+    ordv[0] = -7            # clamps to row 0 (still named)
+    ordv[1] = total + 50    # clamps to the last row (the ragged q-block of the last head): row 1 unnamed
+    ordv[3] = ordv[2]       # row 2 twice, row 3 unnamed
+    named = set(np.clip(ordv, 0, total - 1).tolist())
+    order = torch.from_numpy(ordv).to(device())
+    o = torch.full_like(v, float("nan"))
+    lse = torch.full((wl.outer, wl.N), float("nan"), dtype=torch.float32, device=device())
+    if kind == "fp8":
+        ref, ref_l = t.block_sparse_attn_fp8(q, k, v, cnt, idx, lse=True)
+        t.block_sparse_attn_fp8(q, k, v, cnt, idx, lse=True, order=order, out=o, lse_out=lse)
+    else:
+        ref, ref_l = t.block_sparse_attn(q, k, v, cnt, idx, wl.block_q, wl.block_k, wl.sm_scale, lse=True)
+        t.block_sparse_attn_scheduled(q, k, v, cnt, idx, order, wl.block_q, wl.block_k, wl.sm_scale, lse=True,
+                                      out=o, lse_out=lse)
+    torch.cuda.synchronize()
+    for row in range(total):
+        hd, qb = divmod(row, wl.nqb)
+        sl = slice(qb * wl.block_q, min(wl.N, (qb + 1) * wl.block_q))
+        if row in named:
+            assert torch.equal(o[hd, sl].view(torch.int16), ref[hd, sl].view(torch.int16)), "row %d" % row
+            assert torch.equal(lse[hd, sl], ref_l[hd, sl]), "lse row %d" % row
+        else:
+            assert bool(torch.isnan(o[hd, sl].float()).all()) and bool(torch.isnan(lse[hd, sl]).all()), \
+                "unnamed row %d written" % row
