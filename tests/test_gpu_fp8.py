@@ -145,23 +145,25 @@ def test_fp8_every_list_length(orc):
             assert float(np.abs(oc[h, qb * 128:(qb + 1) * 128]).max()) == 0.0
 
 
-def test_fp8_full_size_sampled(orc):
-    # Wan2.1-14B shape: every head and q-block on the GPU with the GPU mask of seeded entropies;
-    # seeded q-blocks (the ragged last one included) of two seeded heads against the oracle
+@pytest.mark.parametrize("wid", [3, 4])
+def test_fp8_full_size_sampled(orc, wid):
+    # Wan2.1-14B and HunyuanVideo shapes: every head and q-block on the GPU with the GPU mask of
+    # seeded entropies; seeded q-blocks (the ragged last one included) of two seeded heads against
+    # the oracle
     torch = torch_mod()
     t = tra()
-    wl = workloads.get(3)
+    wl = workloads.get(wid)
     say("fp8 sparse full size", wl.name)
     q, k, v = _inputs(wl)
-    ent = synth.entropy_like(730, wl.outer, wl.N)
+    ent = synth.entropy_like(727 + wid, wl.outer, wl.N)
     cnt, idx, _ = t.build_block_mask(torch.from_numpy(ent).to(device()), wl.F, wl.H, wl.W, wl.tau, wl.gamma,
                                      wl.block_q, wl.block_k, wl.vote_threshold)
     qp, kp, vp = _tile_major(t, wl, q, k, v)
     o, L = t.block_sparse_attn_fp8(qp, kp, vp, cnt, idx, lse=True, sm_scale=wl.sm_scale)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o.float()).all())
-    blocks, rows = sample_rows(731, wl.N, 128, 3)
-    heads = synth.uniform_ints(732, 2, 0, wl.outer)
+    blocks, rows = sample_rows(728 + 3 * wid, wl.N, 128, 3)
+    heads = synth.uniform_ints(729 + 3 * wid, 2, 0, wl.outer)
     mask = np.zeros((wl.outer, wl.nqb, wl.nkb), dtype=np.uint8)
     for h in heads:
         mask[h][blocks], _ = orc.block_mask(ent[h], wl.F, wl.H, wl.W, wl.tau, wl.gamma, 128, 64, 1, qblocks=blocks)
