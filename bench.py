@@ -259,7 +259,7 @@ def main():
         return e0.elapsed_time(e1) / reps
 
     reps = max(3, args.steps)
-    ms_dense_plain = ms_reuse_b2b = ms_sparse_b2b = ms_sparse_default = ms_sparse_cold = None
+    ms_dense_plain = ms_reuse_b2b = ms_sparse_b2b = ms_sparse_default = ms_sparse_cold = ms_copy = None
     ms_fused = ms_reuse_nat = ms_dense_nat = ms_fused_nat = None
     if not args.headline_only:
         # the library's dense path without the entropy: the speed-up reference (outside the steps)
@@ -295,6 +295,9 @@ def main():
             cold.append(e0.elapsed_time(e1))
         del scratch
         ms_sparse_cold = float(np.mean(cold))
+        # the runtime's own device-to-device copy of one q-sized tensor: the reference the
+        # permutations are compared with beside the HBM peak
+        ms_copy = timed(lambda: osp.copy_(qp), reps)
         # the warm-up pass with the mask builder fused in (same outputs as dense_entropy + build_mask)
         ms_fused = None
         if wl.dtype == "bf16" and wl.D == 128 and wl.block_q == 128 and not wl.static_mask:
@@ -397,6 +400,7 @@ def main():
     tensor_bytes = wl.outer * wl.N * wl.D * elem
     perm_gbs = 3 * 2 * tensor_bytes / (ms["permute_qkv"] * 1e-3) / 1e9
     unperm_gbs = 2 * tensor_bytes / (ms["unpermute"] * 1e-3) / 1e9
+    copy_gbs = None if ms_copy is None else 2 * tensor_bytes / (ms_copy * 1e-3) / 1e9
     nnz = int(cnt.to(torch.int64).sum().item())
     mask_bytes = 4 * wl.outer * wl.N + 4 * nnz + 4 * wl.outer * wl.nqb
     mask_gbs = mask_bytes / (ms["build_mask"] * 1e-3) / 1e9
@@ -447,9 +451,14 @@ def main():
             "dense_entropy": {"bound": "mfma", "achieved": round(dense_tf, 2), "peak": peak, "unit": "TFLOP/s",
                               "frac": round(dense_tf / peak, 4), "flops_per_launch": dense_flops},
             "permute_qkv": {"bound": "hbm", "achieved": round(perm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                            "frac": round(perm_gbs / PEAK_HBM_GBS, 4), "bytes": 6 * tensor_bytes},
+                            "frac": round(perm_gbs / PEAK_HBM_GBS, 4), "bytes": 6 * tensor_bytes,
+                            "vs_device_copy": None if copy_gbs is None else round(perm_gbs / copy_gbs, 3)},
             "unpermute": {"bound": "hbm", "achieved": round(unperm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                          "frac": round(unperm_gbs / PEAK_HBM_GBS, 4), "bytes": 2 * tensor_bytes},
+                          "frac": round(unperm_gbs / PEAK_HBM_GBS, 4), "bytes": 2 * tensor_bytes,
+                          "vs_device_copy": None if copy_gbs is None else round(unperm_gbs / copy_gbs, 3)},
+            "device_copy": None if copy_gbs is None else {
+                "achieved": round(copy_gbs, 1), "unit": "GB/s", "bytes": 2 * tensor_bytes,
+                "note": "the runtime's device-to-device copy of one q-sized tensor, back to back"},
             "build_mask": {"bound": "alu", "achieved_hbm": round(mask_gbs, 2), "unit": "GB/s", "bytes": mask_bytes,
                            "pct_of_sparse_time": round(100.0 * ms["build_mask"] / ms["sparse_attn"], 2)},
         },

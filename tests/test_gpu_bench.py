@@ -39,3 +39,7 @@ def test_bench_json_line():
     assert f8["ms"] > 0 and abs(f8["frac_blended"] - f8["achieved"] / f8["peak_blended"]) < 1e-3
     m1 = d["mask_1d"]
     assert m1["ms_mask"] > 0 and 0.0 < m1["density"] <= 1.0 and m1["ms_sparse"] > 0
+    rl = d["rooflines"]
+    assert rl["device_copy"]["achieved"] > 0
+    for name in ("permute_qkv", "unpermute"):
+        assert abs(rl[name]["vs_device_copy"] - rl[name]["achieved"] / rl["device_copy"]["achieved"]) < 2e-3
