@@ -62,6 +62,7 @@ def _compare(t, wl, q, k, v, vote):
     (1, 8, 12, 0.05, 0.5, 1),        # one ragged q-block: the workgroup's second half has no row
     (2, 8, 8, 0.05, 0.5, 2),         # exactly one q-block
     (3, 7, 9, 0.05, 0.5, 1),         # N = 189: two q-blocks, the second ragged
+    (64, 2, 4, 0.3, 0.1, 1),         # 64 frames: the most the two split threshold buffers hold
 ])
 def test_fused_small_full(orc, F, H, W, tau, gamma, vote):
     # every query and every q-block of both heads against the oracle, and bit for bit against
@@ -98,4 +99,9 @@ def test_fused_rejects_unsupported():
     q = torch.zeros((1, 4 * 16 * 16, 64), dtype=torch.bfloat16, device=device())
     with pytest.raises(t.TraError) as ei:
         t.dense_attn_entropy_mask(q, q.clone(), q.clone(), 4, 16, 16, 0.03, 0.5)
+    assert ei.value.code == 2
+    # 65 frames: one more than the split threshold buffers hold, refused before any launch
+    q = torch.zeros((1, 65 * 2 * 4, 128), dtype=torch.bfloat16, device=device())
+    with pytest.raises(t.TraError) as ei:
+        t.dense_attn_entropy_mask(q, q.clone(), q.clone(), 65, 2, 4, 0.3, 0.1)
     assert ei.value.code == 2

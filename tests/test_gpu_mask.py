@@ -57,6 +57,29 @@ def test_mask_small_all_blocks(orc, F, H, W, tau, gamma, bq, vote):
     _compare(orc, ent, cnt, idx, msk, F, H, W, tau, gamma, bq, 64, vote, heads=range(2))
 
 
+@pytest.mark.parametrize("bq", [128, 64])
+def test_mask_largest_frame_count(orc, bq):
+    # the most frames the builder's LDS holds for this block_q (per-query thresholds toward every
+    # frame): found by asking the library, which refuses one frame more before any launch; that
+    # grid bit for bit against the oracle, every q-block of both heads
+    t = tra()
+    H, W, tau, gamma = 2, 3, 0.3, 0.2
+    F = 1
+    while True:
+        try:
+            t.mask_prepare(F + 1, H, W, tau, gamma, bq, 64)
+        except t.TraError as e:
+            assert e.code == 2, "expected TRA_ERR_UNSUPPORTED past the largest frame count"
+            break
+        F += 1
+        assert F < 4096
+    say("mask at the largest frame count", F, "frames, block_q", bq)
+    assert F >= 40
+    ent = synth.entropy_like(960 + bq, 2, F * H * W)
+    cnt, idx, msk = _gpu_mask(t, ent, F, H, W, tau, gamma, bq, 64, 1)
+    _compare(orc, ent, cnt, idx, msk, F, H, W, tau, gamma, bq, 64, 1, heads=range(2))
+
+
 @pytest.mark.parametrize("tile", [(1, 1), (3, 5), (4, 16), (16, 16), (2, 8)])
 @pytest.mark.parametrize("F,H,W,tau,gamma,bq,vote", [
     (4, 16, 16, 0.03, 0.5, 128, 1),
