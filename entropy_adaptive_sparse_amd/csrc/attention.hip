@@ -335,13 +335,20 @@ struct NoCopies {
 // same copies as fetch_tile's: tile-major, ksrc / vsrc are the tiles' first bytes; NAT, they
 // are the head's base and natK / natV hold the tiles' row groups (nat_groups).  K rows hold DK
 // bf16 values' worth of bytes (DK = D/2 for fp8 keys), V rows D bf16 values; NPOS S^T products.
-template <int DK, int DV, int NT, bool NAT, int NPOS>
+// BUF: the copies are buffer loads into LDS (MUBUF, the head's K and V as raw buffers, the tile's
+// byte offset in soffset) instead of global_load_lds.  The global form is a FLAT instruction that
+// the compiler's wait-count model takes for a possible LDS access completing out of order, so
+// after one is issued every wait for an LDS operand becomes lgkmcnt(0) and drains all the K reads
+// issued ahead of their products; with buffer loads each product waits for its own operand only.
+template <int DK, int DV, int NT, bool NAT, int NPOS, bool BUF = false>
 struct SpreadCopies {
     using CK = Bf16Cfg<DK, NT>;
     using CV = Bf16Cfg<DV, NT>;
     const char *ksrc, *vsrc;
     lds_char_t *kdst, *vdst;
     int soffK, soffV, natK, natV, w;
+    __amdgpu_buffer_rsrc_t krs, vrs;  // BUF: the head's K and V as raw buffers
+    int kbase, vbase;                 // BUF: byte offsets of the tiles in them
 
     template <bool ISV>
     __device__ inline void copy(int i) const {
@@ -351,6 +358,8 @@ struct SpreadCopies {
         if constexpr (NAT)
             __builtin_amdgcn_global_load_lds((ISV ? vsrc : ksrc) + lane_offset(lane_value(ISV ? natV : natK, i) + so), dst,
                                              16, 0, 0);
+        else if constexpr (BUF)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ISV ? vrs : krs, dst, 16, so, (ISV ? vbase : kbase) + m * 1024, 0, 0);
         else
             __builtin_amdgcn_global_load_lds(uniform_ptr((ISV ? vsrc : ksrc) + m * 1024) + lane_offset(so), dst, 16, 0, 0);
     }
@@ -487,7 +496,11 @@ struct Bf16Kernel {
     using CK = Bf16Cfg<DK, NT>;                 // K tiles
     static_assert(!KF8 || (QW == 1 && !NAT && D == 128), "fp8 keys: one 32-query block per wavefront, D = 128");
     static constexpr int NPOS = KF8 ? 2 * (D / 64) : 2 * (D / 16);  // S^T products per tile
-    using Spread = SpreadCopies<DK, D, NT, NAT, NPOS>;
+    // the tile-major sparse kernels issue their spread copies as buffer loads (the host keeps a
+    // head's K and V under 2^31 bytes); the dense kernels keep the global form, which measured
+    // faster for them (they run at the 256-register limit)
+    static constexpr bool BUF = SPARSE && !NAT;
+    using Spread = SpreadCopies<DK, D, NT, NAT, NPOS, BUF>;
 
     struct Ctx {
         const char *kp, *vp;
@@ -501,6 +514,7 @@ struct Bf16Kernel {
         int koff[D / 16];  // K operand offsets (KF8: the first D / 32)
         int voff[D / 32];
         int soffK, soffV;  // lane offset in copy 0 of a K / V tile (copy_xor gives the others)
+        __amdgpu_buffer_rsrc_t krs, vrs;  // BUF: the head's K and V
         QRegs<D, QW, KF8> qr;
         f32x16_t oacc[D / 32][QW];
         RowState st[QW];
@@ -554,6 +568,9 @@ struct Bf16Kernel {
             const int w = __builtin_amdgcn_readfirstlane(x.wave);
             if constexpr (NAT)
                 cp = Spread{x.kp, x.vp, kd, vd, opaque(x.soffK), opaque(x.soffV), x.natK, x.natV, w};
+            else if constexpr (BUF)
+                cp = Spread{nullptr, nullptr, kd, vd, opaque(x.soffK), opaque(x.soffV), 0, 0, w, x.krs, x.vrs,
+                            x.keyK * CK::ROW, x.keyV * C::ROW};
             else
                 cp = Spread{x.kp + (int64_t)(SPARSE ? x.keyK : key0_full(x, j + 2)) * CK::ROW,
                             x.vp + (int64_t)(SPARSE ? x.keyV : key0_full(x, j + 1)) * C::ROW, kd, vd,
@@ -695,6 +712,12 @@ struct Bf16Kernel {
         // K rows are CK::ROW bytes (D bytes for fp8 keys)
         x.kp = static_cast<const char *>(a.k) + head * (CK::ROW / D);
         x.vp = reinterpret_cast<const char *>(static_cast<const __bf16 *>(a.v) + head);
+        if constexpr (BUF) {
+            // raw buffers over this head's K and V (word 3 for the gfx9 family: 32-bit data format,
+            // no swizzle); num_records = the head's bytes, so the hardware also drops any access past them
+            x.krs = __builtin_amdgcn_make_buffer_rsrc((void *)x.kp, (short)0, N * CK::ROW, 0x00020000);
+            x.vrs = __builtin_amdgcn_make_buffer_rsrc((void *)x.vp, (short)0, N * C::ROW, 0x00020000);
+        }
         const int q0 = qb * BQ + x.wave * 32 * QW + ql;  // query of block 0 (block q2: + 32 q2)
 
         x.natK = x.natV = 0;

@@ -190,6 +190,9 @@ tra_status tra_mask_prepare_1d(int F, int H, int W, float tau, int block_q, int 
  * stays inside q, k, v and the list row, but the result is then unspecified).
  * lse: optional fp32 [outer][N].  With every block retained the result equals
  * tra_dense_attn_entropy's bit for bit (same tile order, same arithmetic).
+ * bf16: each head's K and V are read as raw buffers, so N * D * 2 must stay
+ * below 2^31 bytes (N < 8,388,608 at D = 128); larger returns
+ * TRA_ERR_UNSUPPORTED before any HIP call.
  */
 tra_status tra_block_sparse_attn(const void *q, const void *k, const void *v, void *o, float *lse,
                                  const int32_t *kv_count, const int32_t *kv_index, int outer, int N, int D,
@@ -212,8 +215,8 @@ tra_status tra_block_sparse_attn(const void *q, const void *k, const void *v, vo
  * kv_count / kv_index as for tra_block_sparse_attn (clamped the same way);
  * order: NULL, or a schedule from tra_sparse_schedule (as in
  * tra_block_sparse_attn_scheduled).
- * Supported: D = 128, block_q = 128, block_k = 64; anything else returns
- * TRA_ERR_UNSUPPORTED before any HIP call.
+ * Supported: D = 128, block_q = 128, block_k = 64, N * D * 2 < 2^31 (as for
+ * the bf16 call); anything else returns TRA_ERR_UNSUPPORTED before any HIP call.
  */
 tra_status tra_block_sparse_attn_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
                                      const int32_t *kv_count, const int32_t *kv_index, const int32_t *order,
@@ -248,7 +251,8 @@ tra_status tra_sparse_schedule(const int32_t *kv_count, int outer, int F, int H,
 /*
  * tra_block_sparse_attn with workgroup b running the row order[b] (a schedule
  * written by tra_sparse_schedule for the same kv_count, outer, N, block_q).
- * Results equal tra_block_sparse_attn's bit for bit.  order must be a
+ * Arguments and limits as tra_block_sparse_attn's; results equal it bit for
+ * bit.  order must be a
  * permutation of [0, outer * nqb); other values are clamped into that range
  * (every access stays in bounds, but rows may then be left unwritten).
  */

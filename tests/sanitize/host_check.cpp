@@ -267,6 +267,19 @@ int main() {
         CHECK(tra_block_sparse_attn(q.data(), k.data(), v.data(), o.data(), nullptr, cnt.data(), idx.data(), 1, N, 96,
                                     TRA_BF16, 0.088f, 128, 64, nullptr) == TRA_ERR_UNSUPPORTED,
               "D = 96");
+        // a head's K and V are read as raw buffers: 2^31 bytes or more is refused before any launch
+        // (nothing is read: the stand-in launchers never run for these)
+        const int big = 1 << 23;  // 2^23 tokens x 128 x 2 B = 2^31 B
+        CHECK(tra_block_sparse_attn(q.data(), k.data(), v.data(), o.data(), nullptr, cnt.data(), idx.data(), 1, big, D,
+                                    TRA_BF16, 0.088f, 128, 64, nullptr) == TRA_ERR_UNSUPPORTED,
+              "sparse, 2^31-byte head");
+        CHECK(tra_block_sparse_attn_scheduled(q.data(), k.data(), v.data(), o.data(), nullptr, cnt.data(), idx.data(),
+                                              order.data(), 1, big, D, TRA_BF16, 0.088f, 128, 64,
+                                              nullptr) == TRA_ERR_UNSUPPORTED,
+              "scheduled sparse, 2^31-byte head");
+        CHECK(tra_block_sparse_attn_fp8(q.data(), k.data(), v.data(), o.data(), nullptr, cnt.data(), idx.data(), nullptr,
+                                        1, big, D, 0.088f, 128, 64, nullptr) == TRA_ERR_UNSUPPORTED,
+              "fp8 sparse, 2^31-byte head");
         CHECK(tra_dense_attn_entropy(nullptr, k.data(), v.data(), o.data(), nullptr, nullptr, 1, N, D, TRA_BF16,
                                      0.088f, nullptr) == TRA_ERR_INVALID_ARG,
               "null q");
