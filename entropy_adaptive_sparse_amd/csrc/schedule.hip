@@ -6,7 +6,7 @@
 // Two orders, both permutations of the rows o * nqb + qb:
 //  - longest first (a list-scheduling order): rows sorted by kv_count, largest first, ties by
 //    row.  Workgroups are dispatched in grid order as slots free up, so the shortest rows end the
-//    grid and the tail is short.  Used when the grid is only a few waves of resident workgroups.
+//    grid and the tail is short.  Used when the grid is under two waves of resident workgroups.
 //  - spatial band order: within a head, rows sorted by (row of tiles, frame, position along the
 //    row of tiles) of their centre token -- runs of q-blocks that sit in the same band of the
 //    frame across consecutive frames, whose lists share most of their k-blocks -- cut into runs

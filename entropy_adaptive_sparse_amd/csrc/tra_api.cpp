@@ -449,8 +449,10 @@ tra_status compute_units(int &cus) {
 }
 
 // Grids of fewer than this many waves of resident sparse workgroups (two per compute unit) take the
-// longest-first order: there the tail of unequal rows is a sizeable part of the call.
-constexpr int kLptWaves = 16;
+// longest-first order: there the tail of unequal rows is a sizeable part of the call and there is
+// little locality to keep.  From two waves up the band order's L2 locality is worth more (it ties
+// longest first at 1.5 and 2.5 waves and beats it by 4-7% at 4 and 6 waves).
+constexpr int kLptWaves = 2;
 // Largest nkb the longest-first sort holds in its LDS histogram.
 constexpr int kLptMaxBins = 16383;
 

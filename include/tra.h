@@ -230,7 +230,7 @@ tra_status tra_block_sparse_attn_fp8(const void *q, const void *k, const void *v
  * differ in length).  Writes order[outer * nqb], a permutation of the rows
  * o * nqb + qb, for tra_block_sparse_attn_scheduled and
  * tra_block_sparse_attn_fp8, computed once per mask like kv_index:
- *  - when the grid is fewer than 16 waves of resident workgroups (two per
+ *  - when the grid is fewer than 2 waves of resident workgroups (two per
  *    compute unit): longest first, rows sorted by kv_count, largest first,
  *    ties by row (a list-scheduling order: the shortest rows end the grid);
  *  - otherwise: the spatial band order, within each head the q-blocks sorted

@@ -254,6 +254,17 @@ int main() {
         CHECK(tra_sparse_schedule(cnt.data(), 1, F, H, W, 128, 64, 8, 8, order.data(), nqb, nullptr) == TRA_OK &&
                   g_sched.lpt && g_sched.nqb == nqb && g_sched.nkb == nkb,
               "schedule (longest first)");
+        {
+            // the threshold: under 2 waves of 2 x 256 resident workgroups (1,024 rows) longest first,
+            // from there the band order
+            std::vector<int32_t> cnt_t((size_t)128 * nqb, 2), order_t((size_t)128 * nqb);
+            CHECK(tra_sparse_schedule(cnt_t.data(), 127, F, H, W, 128, 64, 8, 8, order_t.data(),
+                                      (int64_t)order_t.size(), nullptr) == TRA_OK && g_sched.lpt,
+                  "schedule, 1,016 rows: longest first");
+            CHECK(tra_sparse_schedule(cnt_t.data(), 128, F, H, W, 128, 64, 8, 8, order_t.data(),
+                                      (int64_t)order_t.size(), nullptr) == TRA_OK && !g_sched.lpt,
+                  "schedule, 1,024 rows: band order");
+        }
         CHECK(tra_sparse_schedule(cnt.data(), 1, F, H, W, 128, 64, 8, 8, order.data(), nqb - 1, nullptr) ==
                   TRA_ERR_CAPACITY,
               "schedule capacity");
@@ -346,7 +357,7 @@ int main() {
         std::vector<uint16_t> q((size_t)2 * N * D), k(q.size()), v(q.size()), t(q.size()), o(q.size());
         std::vector<float> ent((size_t)2 * N, 6.0f), lse((size_t)2 * N);
         std::vector<int32_t> cnt((size_t)2 * nqb, 3), idx((size_t)2 * nqb * nkb, 0), order((size_t)2 * nqb);
-        const int outer_band = 256;  // 256 x 38 rows: past 16 waves of 2 x 256 workgroups, the band order
+        const int outer_band = 256;  // 256 x 38 rows: past 2 waves of 2 x 256 workgroups, the band order
         std::vector<int32_t> cnt_band((size_t)outer_band * nqb, 3), order_band((size_t)outer_band * nqb);
         CHECK(tra_tile_major_permute(q.data(), t.data(), 2, F, H, W, D, TRA_BF16, 8, 8, nullptr) == TRA_OK, "step permute");
         CHECK(tra_dense_attn_entropy(t.data(), k.data(), v.data(), o.data(), ent.data(), lse.data(), 2, N, D, TRA_BF16,
@@ -380,7 +391,7 @@ int main() {
         CHECK(g_launches - l0 == 12, "step launches");
         CHECK(g_mallocs == m0 && g_copies == c0 && g_attrs == a0, "no allocation, copy or query after prepare");
     }
-    CHECK(g_launches == 24, "launch count");
+    CHECK(g_launches == 26, "launch count");
     std::printf("host sanitize ok\n");
     return 0;
 }

@@ -54,7 +54,7 @@ def _compare_scheduled(t, wl, qp, kp, vp, cnt, idx, order):
 
 
 def test_schedule_longest_first_small_grid():
-    # a few hundred rows: far fewer than 16 waves of resident workgroups -> longest first
+    # a few hundred rows: fewer than 2 waves of resident workgroups -> longest first
     torch = torch_mod()
     t = tra()
     wl = small_workload(800, 6, 30, 52, 128, "bf16", outer=3, tau=0.01)
@@ -81,8 +81,9 @@ def test_schedule_longest_first_small_grid():
 
 @pytest.mark.parametrize("wid", [3, 2])
 def test_schedule_full_size(wid):
-    # Wan2.1-14B (23,640 rows: the band order) and Wan2.1-1.3B (3,072 rows: longest first), with the
-    # GPU masks of the workload entropies; scheduled bf16 and fp8 calls equal the unscheduled ones
+    # Wan2.1-14B (23,640 rows) and Wan2.1-1.3B (3,072 rows): both past 2 waves of resident workgroups,
+    # the band order; with the GPU masks of the workload entropies, scheduled bf16 and fp8 calls equal
+    # the unscheduled ones
     torch = torch_mod()
     t = tra()
     wl = workloads.get(wid)
@@ -96,7 +97,7 @@ def test_schedule_full_size(wid):
     ordv = order.cpu().numpy()
     total = wl.outer * wl.nqb
     assert np.array_equal(np.sort(ordv), np.arange(total))
-    if total >= 16 * 512:
+    if total >= 2 * 512:
         assert np.array_equal(ordv, _band_reference(wl.F, wl.H, wl.W, wl.block_q, wl.outer))
     else:
         c = cnt.cpu().numpy().ravel()
