@@ -497,8 +497,9 @@ struct Bf16Kernel {
     static_assert(!KF8 || (QW == 1 && !NAT && D == 128), "fp8 keys: one 32-query block per wavefront, D = 128");
     static constexpr int NPOS = KF8 ? 2 * (D / 64) : 2 * (D / 16);  // S^T products per tile
     // the tile-major sparse kernels issue their spread copies as buffer loads (the host keeps a
-    // head's K and V under 2^31 bytes); the dense kernels keep the global form, which measured
-    // faster for them (they run at the 256-register limit)
+    // head's K and V under 2^31 bytes).  The dense kernels keep the global form: at the register
+    // limit they run about 1% slower with it.  The natural-order sparse kernel keeps it too: its
+    // per-lane row offsets gain nothing from the buffer form.
     static constexpr bool BUF = SPARSE && !NAT;
     using Spread = SpreadCopies<DK, D, NT, NAT, NPOS, BUF>;
 
@@ -570,7 +571,8 @@ struct Bf16Kernel {
                 cp = Spread{x.kp, x.vp, kd, vd, opaque(x.soffK), opaque(x.soffV), x.natK, x.natV, w};
             else if constexpr (BUF)
                 cp = Spread{nullptr, nullptr, kd, vd, opaque(x.soffK), opaque(x.soffV), 0, 0, w, x.krs, x.vrs,
-                            x.keyK * CK::ROW, x.keyV * C::ROW};
+                            (SPARSE ? x.keyK : key0_full(x, j + 2)) * CK::ROW,
+                            (SPARSE ? x.keyV : key0_full(x, j + 1)) * C::ROW};
             else
                 cp = Spread{x.kp + (int64_t)(SPARSE ? x.keyK : key0_full(x, j + 2)) * CK::ROW,
                             x.vp + (int64_t)(SPARSE ? x.keyV : key0_full(x, j + 1)) * C::ROW, kd, vd,

@@ -558,7 +558,7 @@ tra::AttnArgs attn_args(const void *q, const void *k, const void *v, void *o, fl
 
 // The tile-major bf16 (and fp8-score) sparse kernels read each head's K and V as raw buffers,
 // whose sizes are 32-bit signed byte counts.
-tra_status check_sparse_buffers(int N, int D, tra_dtype dt) {
+tra_status check_head_buffers(int N, int D, tra_dtype dt) {
     if (dt == TRA_BF16 && (int64_t)N * D * 2 > (int64_t)INT32_MAX) return TRA_ERR_UNSUPPORTED;
     return TRA_OK;
 }
@@ -800,7 +800,7 @@ tra_status tra_block_sparse_attn_scheduled(const void *q, const void *k, const v
                                            int block_k, hipStream_t s) {
     tra_status st = check_attn_common(q, k, v, o, outer, N, D, dt, sm_scale);
     if (st != TRA_OK) return st;
-    st = check_sparse_buffers(N, D, dt);
+    st = check_head_buffers(N, D, dt);
     if (st != TRA_OK) return st;
     if (!kv_count || !kv_index || !order) return TRA_ERR_INVALID_ARG;
     if (block_q < 1 || block_k < 1) return TRA_ERR_INVALID_ARG;
@@ -819,7 +819,7 @@ tra_status tra_block_sparse_attn_fp8(const void *q, const void *k, const void *v
     // q and k are one byte per element, v and o bf16: the common checks hold for every one
     tra_status st = check_attn_common(q, k, v, o, outer, N, D, TRA_BF16, sm_scale);
     if (st != TRA_OK) return st;
-    st = check_sparse_buffers(N, D, TRA_BF16);  // v is bf16
+    st = check_head_buffers(N, D, TRA_BF16);  // v is bf16
     if (st != TRA_OK) return st;
     if (!kv_count || !kv_index) return TRA_ERR_INVALID_ARG;
     if (block_q < 1 || block_k < 1) return TRA_ERR_INVALID_ARG;
@@ -835,7 +835,7 @@ tra_status tra_block_sparse_attn(const void *q, const void *k, const void *v, vo
                                  tra_dtype dt, float sm_scale, int block_q, int block_k, hipStream_t s) {
     tra_status st = check_attn_common(q, k, v, o, outer, N, D, dt, sm_scale);
     if (st != TRA_OK) return st;
-    st = check_sparse_buffers(N, D, dt);
+    st = check_head_buffers(N, D, dt);
     if (st != TRA_OK) return st;
     if (!kv_count || !kv_index) return TRA_ERR_INVALID_ARG;
     if (block_q < 1 || block_k < 1) return TRA_ERR_INVALID_ARG;

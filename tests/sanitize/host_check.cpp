@@ -291,6 +291,9 @@ int main() {
         CHECK(tra_block_sparse_attn_fp8(q.data(), k.data(), v.data(), o.data(), nullptr, cnt.data(), idx.data(), nullptr,
                                         1, big, D, 0.088f, 128, 64, nullptr) == TRA_ERR_UNSUPPORTED,
               "fp8 sparse, 2^31-byte head");
+        CHECK(tra_dense_attn_entropy(q.data(), k.data(), v.data(), o.data(), nullptr, nullptr, 1, big, D, TRA_BF16,
+                                     0.088f, nullptr) == TRA_OK,
+              "dense, 2^31-byte head (global loads: no buffer limit)");
         CHECK(tra_dense_attn_entropy(nullptr, k.data(), v.data(), o.data(), nullptr, nullptr, 1, N, D, TRA_BF16,
                                      0.088f, nullptr) == TRA_ERR_INVALID_ARG,
               "null q");
@@ -391,7 +394,7 @@ int main() {
         CHECK(g_launches - l0 == 12, "step launches");
         CHECK(g_mallocs == m0 && g_copies == c0 && g_attrs == a0, "no allocation, copy or query after prepare");
     }
-    CHECK(g_launches == 26, "launch count");
+    CHECK(g_launches == 27, "launch count");
     std::printf("host sanitize ok\n");
     return 0;
 }
