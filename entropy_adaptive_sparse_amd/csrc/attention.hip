@@ -377,22 +377,24 @@ struct SpreadCopies {
 };
 
 // S^T = K Q^T for one 64-key tile and the wavefront's two 32-query blocks: each K operand
-// read from LDS feeds two MFMAs (one per query block); cp.at(n) runs after product n.
+// read from LDS feeds two MFMAs (one per query block).  The two 32-key halves b are separate
+// accumulation chains, issued alternately so that no product waits on the one before it (each
+// chain still sums its products in the same order).  cp.at(n) runs after product n.
 template <int D, int NT, int QW, class Copies = NoCopies>
 __device__ inline void qk_tile(f32x16_t (&s)[2][QW], const lds_char_t *kb, const int (&koff)[D / 16],
                                const bf16x8_t (&qf)[QW][D / 16], const Copies &cp = Copies()) {
     using C = Bf16Cfg<D, NT>;
     const f32x16_t zero = {};
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
+        for (int b = 0; b < 2; ++b) {
             const bf16x8_t av =
                 *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(kb + koff[ks] + b * 32 * C::ROW);
 #pragma unroll
             for (int q2 = 0; q2 < QW; ++q2)
                 s[b][q2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[q2][ks], ks == 0 ? zero : s[b][q2], 0, 0, 0);
-            cp.at(b * (D / 16) + ks);
+            cp.at(2 * ks + b);
         }
     }
 }
@@ -421,7 +423,7 @@ __device__ inline void qk_tile_f8(f32x16_t (&s)[2][1], const lds_char_t *kb, con
             // formats 0, 0: e4m3 for A and B; no block scales (the product is unscaled)
             s[b][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, q8[ks], ks == 0 ? zero : s[b][0], 0, 0, 0, 0,
                                                                       0, 0);
-            cp.at(b * (D / 64) + ks);
+            cp.at(b * (D / 64) + ks);  // chains one after the other: measured faster here than alternated
         }
     }
 }
