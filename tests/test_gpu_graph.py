@@ -1,9 +1,10 @@
 """GPU: the step recorded into a HIP graph.  After the prepare calls no entry point allocates,
 copies between host and device or clears memory, so the whole warm-up step (permute q, k, v;
 dense attention with entropy; mask; schedule; scheduled block-sparse attention; unpermute) and
-the natural-order reuse step can be captured once and replayed.  Every replay, on fresh inputs
-copied into the captured buffers (eager work and a synchronisation before each), equals the same
-calls made eagerly on those inputs bit for bit."""
+the natural-order reuse step can be captured once and replayed, and so can the variants (the
+1D-distance mask, its schedule, the fp8-score sparse call).  Every replay, on fresh inputs copied
+into the captured buffers (eager work and a synchronisation before each), equals the same calls
+made eagerly on those inputs bit for bit."""
 import math
 
 import numpy as np
@@ -99,3 +100,58 @@ def test_step_graph_replays_equal_eager():
         torch.cuda.synchronize()
         assert torch.equal(onat, r_onat), "natural-order reuse o, replay %d" % rep
     assert np.isfinite(o.float().cpu().numpy()).all()
+
+
+def test_variants_graph_replays_equal_eager():
+    # the 1D-distance mask, its schedule and the fp8-score sparse call taking that order, recorded
+    # after tra_mask_prepare_1d: every replay on fresh q, k, v and entropies equals the eager calls
+    torch = torch_mod()
+    t = tra()
+    dev = device()
+    N = F * H * W
+    nqb, nkb = -(-N // 128), -(-N // 64)
+    sc = 1.0 / math.sqrt(D)
+    t.mask_prepare_1d(F, H, W, TAU)
+
+    q8, k8 = (torch.empty((OUTER, N, D), dtype=torch.float8_e4m3fn, device=dev) for _ in range(2))
+    v = torch.empty((OUTER, N, D), dtype=torch.bfloat16, device=dev)
+    o = torch.empty_like(v)
+    ent = torch.empty((OUTER, N), dtype=torch.float32, device=dev)
+    lse = torch.empty((OUTER, N), dtype=torch.float32, device=dev)
+    cnt = torch.empty((OUTER, nqb), dtype=torch.int32, device=dev)
+    idx = torch.zeros((OUTER, nqb, nkb), dtype=torch.int32, device=dev)
+    order = torch.empty((OUTER * nqb,), dtype=torch.int32, device=dev)
+
+    def step():
+        t.build_block_mask_1d(ent, F, H, W, TAU, kv_count=cnt, kv_index=idx)
+        t.sparse_schedule(cnt, F, H, W, out=order)
+        t.block_sparse_attn_fp8(q8, k8, v, cnt, idx, sm_scale=sc, lse=True, order=order, out=o, lse_out=lse)
+
+    def load(seed):
+        qn, kn, vn = _inputs(torch, seed)
+        for dst, src in ((q8, qn), (k8, kn), (v, vn)):
+            dst.copy_(t.tile_major_permute(src, F, H, W).to(dst.dtype))
+        ent.copy_(torch.from_numpy(synth.entropy_like(seed, OUTER, N)).to(dev))
+        torch.cuda.synchronize()
+
+    ref = {}
+    for seed in SEEDS:
+        load(seed)
+        step()
+        torch.cuda.synchronize()
+        ref[seed] = [x.clone() for x in (cnt, idx, order, o, lse)]
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep, seed in enumerate(SEEDS[::-1] + SEEDS):
+        say("variant replay", rep, "seed", seed)
+        load(seed)
+        g.replay()
+        torch.cuda.synchronize()
+        r_cnt, r_idx, r_order, r_o, r_lse = ref[seed]
+        assert _lists_equal(torch, cnt, idx, r_cnt, r_idx), "1D lists, replay %d" % rep
+        assert torch.equal(order, r_order), "schedule, replay %d" % rep
+        assert torch.equal(o.view(torch.int16), r_o.view(torch.int16)), "fp8 sparse o, replay %d" % rep
+        assert torch.equal(lse, r_lse), "fp8 sparse lse, replay %d" % rep
