@@ -1,6 +1,5 @@
 """Shared helpers for the GPU parity tests (inputs from the seeded generator, the
 oracle on the CPU, the HIP path through the C ABI binding)."""
-import math
 import sys
 
 import numpy as np

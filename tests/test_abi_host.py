@@ -1,7 +1,6 @@
 """Host-only checks of the C ABI (no GPU needed): the library loads, exports every
 symbol include/tra.h declares, and rejects bad arguments with its status codes
 before making any HIP call (so these run in a GPU-less container)."""
-import ctypes
 import os
 import re
 

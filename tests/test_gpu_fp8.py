@@ -19,7 +19,7 @@ import numpy as np
 import pytest
 
 from entropy_adaptive_sparse_amd import synth, workloads
-from gpu_util import (LSE_TOL, check_output, device, np64, qkv_inputs, rows_of_blocks, sample_rows, say,
+from gpu_util import (LSE_TOL, check_output, device, np64, qkv_inputs, sample_rows, say,
                       small_workload, torch_mod, tra)
 
 pytestmark = pytest.mark.gpu

@@ -3,7 +3,6 @@ oracle's brute-force (query, key) disk test and token voting ("Token Radius Atte
 for Efficient Video Generation", section 2: Insight I, Insight II, TRA pipeline steps
 2-3).  Both sides take the same fp32 entropy array (from the seeded generator, or the
 oracle's own fp64 entropies rounded to fp32) and the same fp32 tau and gamma."""
-import math
 
 import numpy as np
 import pytest

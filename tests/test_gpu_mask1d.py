@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from entropy_adaptive_sparse_amd import synth, workloads
-from gpu_util import device, sample_rows, say, small_workload, torch_mod, tra
+from gpu_util import device, sample_rows, say, torch_mod, tra
 
 pytestmark = pytest.mark.gpu
 
