@@ -133,7 +133,8 @@ def rows_of_blocks(blocks, N, bq):
 def check_warmup_against_oracle(orc, wl, qkv_cpu, out, heads, blocks, vote, natural):
     """out = (o, entropy, lse, kv_count, kv_index, block_mask) of a fused warm-up call (GPU tensors;
     o in natural order when `natural`, everything else by tile-major position); qkv_cpu: the
-    natural-order inputs.  Checks the q-blocks `blocks` of the heads `heads` against the oracle."""
+    natural-order inputs.  Checks the q-blocks `blocks` of the heads `heads` against the oracle;
+    returns the oracle's mask bounds (lo, hi) of those rows, one pair per head."""
     torch = torch_mod()
     o, Hh, L, cnt, idx, msk = out
     qc, kc, vc = qkv_cpu
@@ -142,6 +143,7 @@ def check_warmup_against_oracle(orc, wl, qkv_cpu, out, heads, blocks, vote, natu
     nat = perm[rows].astype(np.int64)
     open_entries = 0
     worst = [0.0, 0.0, 0.0]
+    bounds = []
     for h in heads:
         ro, rH, rL = orc.attention(np64(qc[h]), np64(kc[h]), np64(vc[h]), wl.sm_scale, rows=nat.astype(np.int32))
         sel = torch.from_numpy(nat if natural else rows.astype(np.int64)).to(o.device)
@@ -152,9 +154,11 @@ def check_warmup_against_oracle(orc, wl, qkv_cpu, out, heads, blocks, vote, natu
         assert e_ent <= ENT_TOL, "head %d entropy err %.3g" % (h, e_ent)
         assert e_lse <= LSE_TOL, "head %d lse err %.3g" % (h, e_lse)
         lo, hi = mask_bounds(orc, wl, rH, rows, blocks, vote)
+        bounds.append((lo, hi))
         b = torch.from_numpy(np.asarray(blocks, dtype=np.int64)).to(o.device)
         open_entries += check_mask_rows(msk[h].index_select(0, b).cpu().numpy(), cnt[h].index_select(0, b).cpu().numpy(),
                                         idx[h].index_select(0, b).cpu().numpy(), lo, hi, "head %d" % h)
         worst = [max(worst[0], err), max(worst[1], e_ent), max(worst[2], e_lse)]
     say("  vs oracle: max-abs out %.3g, entropy %.3g, lse %.3g; mask entries left open by the entropy "
         "tolerance: %d of %d" % (*worst, open_entries, len(heads) * len(blocks) * wl.nkb))
+    return bounds

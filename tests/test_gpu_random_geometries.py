@@ -6,15 +6,21 @@ seed, then checks on two heads:
   - the mask, counts and index lists bit for bit against the oracle's brute force;
   - the scheduled block-sparse attention (bf16, D = 128) on those lists against the oracle's
     masked attention on every query, at the bf16 tolerances, with lse within 1e-3.
-The fixed cases elsewhere pin the shapes that matter most; these reach combinations nobody
-chose by hand."""
+The same for the fused warm-up, tile-major and natural order (o, entropy, lse within the
+tolerances; mask rows between the oracle's masks from its own entropies moved by the entropy
+tolerance), and the natural-order sparse call on the natural fused call's lists (bit for
+bit the tile-major call; against the oracle, under the oracle's mask, on every q-block whose
+mask row the oracle fixes).  The fixed
+cases elsewhere pin the shapes that matter most; these reach combinations nobody chose by
+hand."""
 import math
 
 import numpy as np
 import pytest
 
-from entropy_adaptive_sparse_amd import synth
-from gpu_util import LSE_TOL, check_output, device, say, torch_mod, tra
+from entropy_adaptive_sparse_amd import synth, workloads
+from gpu_util import (LSE_TOL, check_output, check_warmup_against_oracle, device, np64, qkv_inputs, rows_of_blocks, say,
+                      torch_mod, tra)
 
 pytestmark = pytest.mark.gpu
 
@@ -85,3 +91,61 @@ def test_random_geometry_mask_and_sparse(orc, seed):
         e_lse = float(np.max(np.abs(L_h[h] - rL)))
         assert e_lse <= LSE_TOL, "head %d lse err %.3g" % (h, e_lse)
     say("  sparse max-abs %.3g" % worst)
+
+
+@pytest.mark.parametrize("seed", range(1100, 1108))
+def test_random_geometry_fused_warmup(orc, seed):
+    # the fused warm-up (tile-major on even seeds; natural order on odd ones, then the natural-order
+    # sparse call on its lists) against the oracle: o, entropy and lse within the tolerances, the
+    # mask rows between the oracle's masks from its own entropies moved by the entropy tolerance
+    torch = torch_mod()
+    t = tra()
+    dev = device()
+    F, H, W, th, tw, _, vote, tau, gamma = _case(seed)
+    natural = seed % 2 == 1
+    if natural:  # the natural-order calls move rows in runs of four
+        W = min(40, -(-W // 4) * 4)
+        tw = min(16, -(-tw // 4) * 4)
+    wl = workloads.Workload(seed, "random-%dx%dx%d" % (F, H, W), 1, OUTER, D, "bf16", F, H, W, 128, 64, tau, gamma,
+                            vote, th, tw)
+    say("random fused warm-up", seed, (F, H, W), "tile", (th, tw), "vote", vote, "tau %.4g gamma %.3g" % (tau, gamma),
+        "natural" if natural else "tile-major")
+    q, k, v = qkv_inputs(wl)
+    if natural:
+        qd, kd, vd = (x.to(dev) for x in (q, k, v))
+        out = t.dense_attn_entropy_mask_natural(qd, kd, vd, F, H, W, tau, gamma, wl.sm_scale, 128, 64, vote, th, tw,
+                                                entropy=True, lse=True, want_mask=True)
+    else:
+        qd, kd, vd = (t.tile_major_permute(x.to(dev), F, H, W, th, tw) for x in (q, k, v))
+        out = t.dense_attn_entropy_mask(qd, kd, vd, F, H, W, tau, gamma, wl.sm_scale, 128, 64, vote, th, tw,
+                                        entropy=True, lse=True, want_mask=True)
+    torch.cuda.synchronize()
+    bounds = check_warmup_against_oracle(orc, wl, (q, k, v), out, range(OUTER), np.arange(wl.nqb), vote, natural)
+    if natural:
+        # the reuse step on those lists, natural order in and out: bit for bit the tile-major sparse
+        # call on the permuted tensors, and, on the q-blocks whose mask rows the oracle's own entropies
+        # fix, within the bf16 tolerances of the oracle's masked attention under the oracle's mask
+        _, _, _, cnt, idx, _ = out
+        o, L = t.block_sparse_attn_natural(qd, kd, vd, cnt, idx, F, H, W, 128, 64, wl.sm_scale, lse=True, tile_h=th,
+                                           tile_w=tw)
+        qp, kp, vp = (t.tile_major_permute(x, F, H, W, th, tw) for x in (qd, kd, vd))
+        o2, L2 = t.block_sparse_attn(qp, kp, vp, cnt, idx, 128, 64, wl.sm_scale, lse=True)
+        o2 = t.tile_major_unpermute(o2, F, H, W, th, tw)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "natural vs tile-major sparse o"
+        assert torch.equal(L, L2), "natural vs tile-major sparse lse"
+        perm = orc.tile_major_order(F, H, W, th, tw)
+        o_h, L_h = o.float().cpu().numpy(), L.cpu().numpy()
+        for h, (lo, hi) in zip(range(OUTER), bounds):
+            # the q-blocks whose mask rows the oracle's entropies fix exactly (all but a rare row
+            # with an entry the entropy tolerance leaves open)
+            fixed = [qb for qb in range(wl.nqb) if np.array_equal(lo[qb], hi[qb])]
+            if not fixed:
+                continue
+            rows = rows_of_blocks(fixed, wl.N, 128)
+            qh, kh, vh = (orc.permute(np64(x[h]), perm) for x in (q, k, v))
+            ro, _, rL = orc.attention(qh, kh, vh, wl.sm_scale, rows=rows, block_mask=lo, bq=128, bk=64)
+            err, _ = check_output(o_h[h][perm][rows], ro, "bf16")
+            e_lse = float(np.max(np.abs(L_h[h][rows] - rL)))
+            assert e_lse <= LSE_TOL, "head %d natural sparse lse err %.3g" % (h, e_lse)
+            say("  head %d natural sparse, %d of %d q-blocks fixed: max-abs %.3g" % (h, len(fixed), wl.nqb, err))
