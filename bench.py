@@ -313,8 +313,8 @@ def main():
             torch.cuda.synchronize()
             ms_fused = e0.elapsed_time(e1) / 2
 
-        # the permutation folded into the attention kernels (natural-order q, k, v, o; same results
-        # bit for bit): a reuse step is then one call, a warm-up one dense call plus the mask
+        # the permutation folded into the attention kernels (natural-order q, k, v, o): a reuse step
+        # is then one call, a warm-up one dense call plus the mask
         ms_reuse_nat = ms_dense_nat = ms_fused_nat = None
         if wl.dtype == "bf16" and wl.D == 128 and wl.block_q == 128 and wl.W % 4 == 0 and wl.tile_w % 4 == 0:
             def sparse_nat():

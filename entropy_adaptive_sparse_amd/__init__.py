@@ -411,8 +411,8 @@ def block_sparse_attn_scheduled(q, k, v, kv_count, kv_index, order, block_q: int
 def dense_attn_entropy_natural(q, k, v, F: int, H: int, W: int, sm_scale: float | None = None, entropy: bool = True,
                                lse: bool = False, tile_h: int = 8, tile_w: int = 8, out=None, ent_out=None,
                                lse_out=None):
-    """dense_attn_entropy on natural-order q, k, v; o in natural order, H and lse indexed by tile-major
-    position.  Returns (o, H, lse)."""
+    """dense_attn_entropy on natural-order q, k, v (the sums over keys taken in natural order); o in
+    natural order, H and lse indexed by tile-major position.  Returns (o, H, lse)."""
     torch = _torch()
     outer, N, D = _check_qkv(q, k, v)
     if N != F * H * W:

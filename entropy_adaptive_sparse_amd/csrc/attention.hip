@@ -29,9 +29,10 @@
 // heads together, each on runs of neighbouring q-blocks.  The warm-up variant
 // attn_mask_kernel ends with the mask builder (mask_impl.h) for its own q-block, run in
 // the freed tile buffers (TRA pipeline steps 2-3 fused into the entropy pass).  The NAT
-// instantiations read natural-order q, k, v and write natural-order o through the
-// tile-major map (pipeline step 3's layout applied inside the copies), bit for bit the
-// results of the tile-major kernels on permuted tensors.
+// instantiations read natural-order q, k, v and write natural-order o, with the
+// tile-major map (pipeline step 3's layout) applied to the query and output rows, and in
+// the sparse one to the K and V copies too (bit for bit the tile-major kernel on permuted
+// tensors); the dense ones take K and V in natural order.
 #include "mask_impl.h"
 #include "tra_internal.h"
 
@@ -475,9 +476,13 @@ __device__ inline float tile_max(const f32x16_t (&s)[2][QW], int q2, float c) {
 //   c. the max of tile j+1 (taken before its masking: keys past N are clamped duplicates
 //      of a real key and cannot raise it)
 //
-// NAT: q, k, v and o are in natural token order and are read and written through the
-// tile-major map (nat4); the entropy and lse stay indexed by tile-major position, and the
-// arithmetic is that of the tile-major kernel on the permuted tensors, bit for bit.
+// NAT: q, k, v and o are in natural token order; the entropy and lse stay indexed by
+// tile-major position.  Queries and outputs go through the tile-major map (nat4).  The
+// sparse kernel copies K and V through it too (NATKV: its block lists name tile-major
+// k-blocks), so its arithmetic is that of the tile-major kernel on the permuted tensors, bit
+// for bit.  A dense kernel sums over every key, in any order: the natural-order dense kernels
+// take K and V as they lie, in natural row order, with the tile-major kernel's copies; only
+// the rounding order of the sums differs from the tile-major kernel's.
 // KF8: q and k are fp8 (OCP e4m3, one byte per element), S^T on the fp8 matrix cores (qk_tile_f8);
 // v and o stay bf16 and everything after S^T is unchanged.  K rows are then D bytes: the tile
 // configuration of a D/2-wide bf16 row (DK).
@@ -503,7 +508,8 @@ struct Bf16Kernel {
     // limit they run about 1% slower with it.  The natural-order sparse kernel keeps it too: its
     // per-lane row offsets gain nothing from the buffer form.
     static constexpr bool BUF = SPARSE && !NAT;
-    using Spread = SpreadCopies<DK, D, NT, NAT, NPOS, BUF>;
+    static constexpr bool NATKV = NAT && SPARSE;  // K and V copied through the map
+    using Spread = SpreadCopies<DK, D, NT, NATKV, NPOS, BUF>;
 
     struct Ctx {
         const char *kp, *vp;
@@ -564,12 +570,12 @@ struct Bf16Kernel {
     template <bool FAST>
     static __device__ inline void step(Ctx &x, int j, lds_char_t *kn, lds_char_t *kd, lds_char_t *vc,
                                        lds_char_t *vd, f32x16_t (&s)[2][QW], f32x16_t (&sn)[2][QW]) {
-        int natn = 0;  // NAT: groups of tile j + 3, the K copy of the next step
-        if constexpr (NAT) natn = nat_groups<D, NT>(x.nat4v, key0_full(x, min(j + 3, x.ntiles - 1)), x.N, x.wave, x.lane);
+        int natn = 0;  // NATKV: groups of tile j + 3, the K copy of the next step
+        if constexpr (NATKV) natn = nat_groups<D, NT>(x.nat4v, key0_full(x, min(j + 3, x.ntiles - 1)), x.N, x.wave, x.lane);
         Spread cp{};
         if constexpr (FAST) {
             const int w = __builtin_amdgcn_readfirstlane(x.wave);
-            if constexpr (NAT)
+            if constexpr (NATKV)
                 cp = Spread{x.kp, x.vp, kd, vd, opaque(x.soffK), opaque(x.soffV), x.natK, x.natV, w};
             else if constexpr (BUF)
                 cp = Spread{nullptr, nullptr, kd, vd, opaque(x.soffK), opaque(x.soffV), 0, 0, w, x.krs, x.vrs,
@@ -581,9 +587,9 @@ struct Bf16Kernel {
                             opaque(x.soffK), opaque(x.soffV), 0, 0, w};
         } else {
             if (j + 2 < x.ntiles)
-                fetch_tile<DK, NT, false, NAT>(x.kp, x.nat4, x.natK, key0_of(x, j + 2), x.N, kd, x.soffK, x.wave, x.lane);
+                fetch_tile<DK, NT, false, NATKV>(x.kp, x.nat4, x.natK, key0_of(x, j + 2), x.N, kd, x.soffK, x.wave, x.lane);
             if (j + 1 < x.ntiles)
-                fetch_tile<D, NT, true, NAT>(x.vp, x.nat4, x.natV, key0_of(x, j + 1), x.N, vd, x.soffV, x.wave, x.lane);
+                fetch_tile<D, NT, true, NATKV>(x.vp, x.nat4, x.natV, key0_of(x, j + 1), x.N, vd, x.soffV, x.wave, x.lane);
         }
 
         // a.
@@ -653,7 +659,7 @@ struct Bf16Kernel {
             // c.
             x.mt[q2] = tile_max<QW>(sn, q2, c);
         }
-        if constexpr (NAT) {
+        if constexpr (NATKV) {
             x.natV = x.natK;
             x.natK = natn;
         }
@@ -790,8 +796,8 @@ struct Bf16Kernel {
                 x.voff[db] = row * C::ROW + 64 * (db ^ sel) + 16 * u + 8 * (i & 1);
         }
         {
-            // copy 0's slots: row lane / NCH, chunk lane % NCH; for NAT the row counts within the
-            // copy's run of four natural rows, which is the same number
+            // copy 0's slots: row lane / NCH, chunk lane % NCH; for NATKV the row counts within
+            // the copy's run of four natural rows, which is the same number
             const int rk = lane / CK::NCH, pk = lane % CK::NCH;
             x.soffK = rk * CK::ROW + ((pk ^ CK::fK(rk)) << 4);
             const int row = lane / C::NCH, p = lane % C::NCH;
@@ -817,15 +823,15 @@ struct Bf16Kernel {
         if (x.ntiles > 0) {
             const int k0 = key0_of(x, 0);
             int n0 = 0;
-            if constexpr (NAT) {
+            if constexpr (NATKV) {
                 n0 = nat_groups<D, NT>(x.nat4v, k0, N, x.wave, lane);
                 x.natV = nat_groups<D, NT>(x.nat4v, key0_full(x, min(1, x.ntiles - 1)), N, x.wave, lane);
                 x.natK = nat_groups<D, NT>(x.nat4v, key0_full(x, min(2, x.ntiles - 1)), N, x.wave, lane);
             }
-            fetch_tile<DK, NT, false, NAT>(x.kp, x.nat4, n0, k0, N, K0, x.soffK, x.wave, lane);
-            fetch_tile<D, NT, true, NAT>(x.vp, x.nat4, n0, k0, N, V0, x.soffV, x.wave, lane);
+            fetch_tile<DK, NT, false, NATKV>(x.kp, x.nat4, n0, k0, N, K0, x.soffK, x.wave, lane);
+            fetch_tile<D, NT, true, NATKV>(x.vp, x.nat4, n0, k0, N, V0, x.soffV, x.wave, lane);
             if (x.ntiles > 1)
-                fetch_tile<DK, NT, false, NAT>(x.kp, x.nat4, x.natV, key0_of(x, 1), N, K1, x.soffK, x.wave, lane);
+                fetch_tile<DK, NT, false, NATKV>(x.kp, x.nat4, x.natV, key0_of(x, 1), N, K1, x.soffK, x.wave, lane);
             wait_dma();
             __syncthreads();
             qk(x, s0, K0, Spread{}, std::integral_constant<bool, false>());
@@ -833,20 +839,16 @@ struct Bf16Kernel {
             for (int q2 = 0; q2 < QW; ++q2) x.mt[q2] = tile_max<QW>(s0, q2, x.c);
             __syncthreads();  // every wavefront is done with K_0 before K_2 overwrites it
             int j = 0;
-            // The natural-order dense + entropy kernels keep the step-start copies: the spread
-            // ones would push their registers into spilling.
-            if constexpr (!(NAT && ENT)) {
-                if constexpr (SPARSE && !NAT) {
-                    if (x.ntiles > 4) {
-                        x.keyV = key0_full(x, 1);
-                        x.keyK = key0_full(x, 2);
-                    }
+            if constexpr (SPARSE && !NAT) {
+                if (x.ntiles > 4) {
+                    x.keyV = key0_full(x, 1);
+                    x.keyK = key0_full(x, 2);
                 }
-                // pairs of steps j, j + 1 with j + 4 < ntiles are fast (sparse_fast_steps)
-                for (; j + 4 < x.ntiles; j += 2) {
-                    step<true>(x, j, K1, K0, V0, V1, s0, s1);
-                    step<true>(x, j + 1, K0, K1, V1, V0, s1, s0);
-                }
+            }
+            // pairs of steps j, j + 1 with j + 4 < ntiles are fast (sparse_fast_steps)
+            for (; j + 4 < x.ntiles; j += 2) {
+                step<true>(x, j, K1, K0, V0, V1, s0, s1);
+                step<true>(x, j + 1, K0, K1, V1, V0, s1, s0);
             }
             for (; j < x.ntiles; j += 2) {
                 step<false>(x, j, K1, K0, V0, V1, s0, s1);

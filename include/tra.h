@@ -292,14 +292,20 @@ tra_status tra_dense_attn_entropy_mask(const void *q, const void *k, const void 
  * permutation folded into their loads and stores (pipeline step 3: the
  * tile-major layout keeps spatial neighbours contiguous; here it is applied
  * while the kernels copy rows, so no permuted copy of q, k, v or o exists).
+ * o is written in natural order, while entropy and lse (each may be NULL)
+ * stay indexed by TILE-MAJOR position, the order tra_build_block_mask reads,
+ * and kv_count / kv_index are the tile-major block lists it writes.
  *
- * Results equal, bit for bit,
- *   tra_tile_major_permute of q, k, v; the tile-major call; and
+ * The sparse call equals, bit for bit,
+ *   tra_tile_major_permute of q, k, v; tra_block_sparse_attn; and
  *   tra_tile_major_unpermute of o,
- * for the same tile_h, tile_w: o is written in natural order, while entropy
- * and lse (each may be NULL) stay indexed by TILE-MAJOR position, the order
- * tra_build_block_mask reads, and kv_count / kv_index are the tile-major
- * block lists tra_build_block_mask writes.
+ * for the same tile_h, tile_w.  The dense calls (below and the fused one) see
+ * every key, so they read k and v as they lie and sum over the keys in natural
+ * order: they equal, bit for bit, the tile-major call on permuted q with k
+ * and v unpermuted, o unpermuted; against the fully permuted chain only the
+ * rounding order of those sums differs (the results agree within the
+ * attention tolerances, not bit for bit, and a mask entry whose entropy sits
+ * on a threshold may differ with it).
  *
  * q, k, v, o: device, [outer][N][128] bf16, natural order, N = F*H*W.  The
  * sparse call takes its rows in the spatial band order of tra_sparse_schedule
@@ -315,9 +321,10 @@ tra_status tra_dense_attn_entropy_mask(const void *q, const void *k, const void 
  */
 /*
  * tra_dense_attn_entropy_mask on natural-order q, k, v, o (the warm-up step in one call):
- * results equal tra_dense_attn_entropy_mask on the permuted tensors bit for bit, with o
- * unpermuted; entropy, lse and the block lists are tile-major.  Supported: the intersection
- * of what the two calls above support.
+ * results equal tra_dense_attn_entropy_mask on permuted q and natural-order k, v bit for bit,
+ * with o unpermuted (the keys in natural order, as above); entropy, lse and the block lists
+ * are tile-major, the lists those tra_build_block_mask writes from this call's entropies.
+ * Supported: the intersection of what the two calls above support.
  */
 tra_status tra_dense_attn_entropy_mask_natural(const void *q, const void *k, const void *v, void *o, float *entropy,
                                                float *lse, int outer, int F, int H, int W, int D, tra_dtype dt,

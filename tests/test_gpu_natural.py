@@ -7,7 +7,9 @@ Each call is compared
   oracle's fp64 attention (dense, or restricted to the oracle's block mask), entropy and lse
   by tile-major position; the fused warm-up's mask rows between the oracle's bounds
   (gpu_util.mask_bounds) -- on small grids in full and on seeded q-blocks at full size;
-- with the permute -> tile-major call -> unpermute chain, bit for bit.
+- bit for bit with tile-major calls: the sparse call with the permute -> tile-major call ->
+  unpermute chain; the dense calls (which sum over the keys in natural order) with the
+  tile-major call on permuted q and natural-order k, v, o unpermuted.
 """
 import dataclasses
 
@@ -32,11 +34,12 @@ def _bits(x):
 
 
 def _compare(t, wl, q, k, v):
-    """natural calls vs the permuted chain; returns the natural dense outputs and the lists"""
+    """natural calls vs tile-major calls, bit for bit; returns the natural dense outputs"""
     torch = torch_mod()
     F, H, W, th, tw = wl.F, wl.H, wl.W, wl.tile_h, wl.tile_w
     qp, kp, vp = (t.tile_major_permute(x, F, H, W, th, tw) for x in (q, k, v))
-    o1, h1, l1 = t.dense_attn_entropy(qp, kp, vp, wl.sm_scale, entropy=True, lse=True)
+    # dense: the tile-major kernel on permuted q with k, v as given (keys in natural order)
+    o1, h1, l1 = t.dense_attn_entropy(qp, k, v, wl.sm_scale, entropy=True, lse=True)
     o1n = t.tile_major_unpermute(o1, F, H, W, th, tw)
     o2, h2, l2 = t.dense_attn_entropy_natural(q, k, v, F, H, W, wl.sm_scale, entropy=True, lse=True, tile_h=th,
                                               tile_w=tw)
@@ -45,11 +48,12 @@ def _compare(t, wl, q, k, v):
     assert torch.equal(h1, h2), "entropy"
     assert torch.equal(l1, l2), "lse"
     # entropy off: the kernel without the entropy sums
-    o3, _, _ = t.dense_attn_entropy(qp, kp, vp, wl.sm_scale, entropy=False)
+    o3, _, _ = t.dense_attn_entropy(qp, k, v, wl.sm_scale, entropy=False)
     o4, _, _ = t.dense_attn_entropy_natural(q, k, v, F, H, W, wl.sm_scale, entropy=False, tile_h=th, tile_w=tw)
     assert torch.equal(_bits(t.tile_major_unpermute(o3, F, H, W, th, tw)), _bits(o4)), "dense o (no entropy)"
 
-    cnt, idx, _ = t.build_block_mask(h1, F, H, W, wl.tau, wl.gamma, wl.block_q, wl.block_k, wl.vote_threshold,
+    # sparse: the permuted chain
+    cnt, idx, _ = t.build_block_mask(h2, F, H, W, wl.tau, wl.gamma, wl.block_q, wl.block_k, wl.vote_threshold,
                                      th, tw)
     s1, sl1 = t.block_sparse_attn(qp, kp, vp, cnt, idx, wl.block_q, wl.block_k, wl.sm_scale, lse=True)
     s2, sl2 = t.block_sparse_attn_natural(q, k, v, cnt, idx, F, H, W, wl.block_q, wl.block_k, wl.sm_scale, lse=True,
@@ -58,7 +62,7 @@ def _compare(t, wl, q, k, v):
     assert torch.equal(_bits(t.tile_major_unpermute(s1, F, H, W, th, tw)), _bits(s2)), "sparse o"
     assert torch.equal(sl1, sl2), "sparse lse"
     say("  block density %.3f" % float(cnt.float().sum().item() / (cnt.shape[0] * cnt.shape[1] * idx.shape[2])))
-    return o2, h2
+    return o2, h2, l2
 
 
 @pytest.mark.parametrize("F,H,W,tile", [
@@ -71,12 +75,32 @@ def _compare(t, wl, q, k, v):
     (1, 4, 8, (8, 8)),        # N = 32: one ragged tile
     (1, 1, 4, (8, 8)),        # N = 4: one run of four rows
 ])
-def test_natural_equals_permuted_chain(F, H, W, tile):
+def test_natural_equals_tile_major_calls(orc, F, H, W, tile):
+    # bit for bit the tile-major calls; the dense outputs of every query of both heads against
+    # the oracle
     t = tra()
     wl = _wl(300 + F + H + W, F, H, W, tile)
     say("natural order", F, H, W, tile)
-    q, k, v = (x.to(device()) for x in qkv_inputs(wl))
-    _compare(t, wl, q, k, v)
+    qc, kc, vc = qkv_inputs(wl)
+    o, ent, lse = _compare(t, wl, qc.to(device()), kc.to(device()), vc.to(device()))
+    _check_dense_natural(orc, wl, (qc, kc, vc), o, ent, lse)
+
+
+def _check_dense_natural(orc, wl, qkv, o, ent, lse):
+    """natural-order dense outputs (o natural, entropy and lse tile-major) of every query of
+    every head against the oracle"""
+    o, ent, lse = o.float().cpu().numpy(), ent.cpu().numpy(), lse.cpu().numpy()
+    perm = orc.tile_major_order(wl.F, wl.H, wl.W, wl.tile_h, wl.tile_w)
+    worst = [0.0, 0.0, 0.0]
+    for h in range(wl.outer):
+        ro, rH, rL = orc.attention(*(np64(x[h]) for x in qkv), wl.sm_scale)
+        err, _ = check_output(o[h], ro, "bf16")                    # natural order
+        e_ent = float(np.max(np.abs(ent[h] - rH[perm])))           # tile-major order
+        e_lse = float(np.max(np.abs(lse[h] - rL[perm])))
+        assert e_ent <= 1e-3, "head %d entropy err %.3g" % (h, e_ent)
+        assert e_lse <= LSE_TOL, "head %d lse err %.3g" % (h, e_lse)
+        worst = [max(worst[0], err), max(worst[1], e_ent), max(worst[2], e_lse)]
+    say("  natural dense vs oracle: max-abs out %.3g, entropy %.3g, lse %.3g" % tuple(worst))
 
 
 def test_natural_sparse_every_list_length():
@@ -127,9 +151,10 @@ def test_natural_fused_warmup(orc, F, H, W, tile, vote):
     qkv = qkv_inputs(wl)
     q, k, v = (x.to(device()) for x in qkv)
     th, tw = tile
-    qp, kp, vp = (t.tile_major_permute(x, F, H, W, th, tw) for x in (q, k, v))
+    qp = t.tile_major_permute(q, F, H, W, th, tw)
     args = (F, H, W, wl.tau, wl.gamma, wl.sm_scale, wl.block_q, wl.block_k, vote, th, tw)
-    o1, h1, l1, c1, i1, m1 = t.dense_attn_entropy_mask(qp, kp, vp, *args, lse=True, want_mask=True)
+    # bit for bit the tile-major fused call on permuted q with k, v as given (keys in natural order)
+    o1, h1, l1, c1, i1, m1 = t.dense_attn_entropy_mask(qp, k, v, *args, lse=True, want_mask=True)
     o2, h2, l2, c2, i2, m2 = t.dense_attn_entropy_mask_natural(q, k, v, *args, lse=True, want_mask=True)
     torch.cuda.synchronize()
     assert torch.equal(_bits(t.tile_major_unpermute(o1, F, H, W, th, tw)), _bits(o2)), "o"
@@ -250,21 +275,6 @@ def test_natural_sparse_full_size_against_oracle(orc):
     _check_sparse_natural(orc, wl, qkv, o, L, mask, heads, blocks)
 
 
-def test_natural_against_oracle(orc):
-    t = tra()
-    wl = _wl(333, 3, 15, 20)
-    say("natural order vs oracle", wl.F, wl.H, wl.W)
-    qc, kc, vc = qkv_inputs(wl)
-    o, ent = _compare(t, wl, qc.to(device()), kc.to(device()), vc.to(device()))
-    o = o.float().cpu().numpy()
-    ent = ent.cpu().numpy()
-    perm = orc.tile_major_order(wl.F, wl.H, wl.W)
-    for h in range(wl.outer):
-        ro, rH, _ = orc.attention(*(x[h].float().numpy().astype(np.float64) for x in (qc, kc, vc)), wl.sm_scale)
-        check_output(o[h], ro, "bf16")                              # natural order
-        assert float(np.max(np.abs(ent[h] - rH[perm]))) <= 1e-3      # tile-major order
-
-
 def test_natural_full_size_workload3():
     torch = torch_mod()
     t = tra()
@@ -272,8 +282,17 @@ def test_natural_full_size_workload3():
     say("natural order at full size", wl.name)
     q, k, v = (x.to(device()) for x in qkv_inputs(wl))
     F, H, W = wl.F, wl.H, wl.W
-    qp, kp, vp = (t.tile_major_permute(x, F, H, W) for x in (q, k, v))
-    o1, h1, _ = t.dense_attn_entropy(qp, kp, vp, wl.sm_scale, entropy=True)
+    qp = t.tile_major_permute(q, F, H, W)
+    # dense: the tile-major call on permuted q and natural-order k, v
+    o1, h1, _ = t.dense_attn_entropy(qp, k, v, wl.sm_scale, entropy=True)
+    o1n = t.tile_major_unpermute(o1, F, H, W)
+    d2, h2, _ = t.dense_attn_entropy_natural(q, k, v, F, H, W, wl.sm_scale, entropy=True)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2), "entropy at full size"
+    assert torch.equal(_bits(o1n), _bits(d2)), "dense o at full size"
+    del o1n, d2
+    # sparse: the permuted chain
+    kp, vp = (t.tile_major_permute(x, F, H, W) for x in (k, v))
     cnt, idx, _ = t.build_block_mask(h1, F, H, W, wl.tau, wl.gamma, wl.block_q, wl.block_k, wl.vote_threshold)
     s1, _ = t.block_sparse_attn(qp, kp, vp, cnt, idx, wl.block_q, wl.block_k, wl.sm_scale, out=o1)
     del qp, kp, vp
@@ -282,10 +301,6 @@ def test_natural_full_size_workload3():
     s2, _ = t.block_sparse_attn_natural(q, k, v, cnt, idx, F, H, W, wl.block_q, wl.block_k, wl.sm_scale)
     torch.cuda.synchronize()
     assert torch.equal(_bits(s1n), _bits(s2)), "sparse o at full size"
-    del s1n, s2
-    d2, h2, _ = t.dense_attn_entropy_natural(q, k, v, F, H, W, wl.sm_scale, entropy=True)
-    torch.cuda.synchronize()
-    assert torch.equal(h1, h2), "entropy at full size"
 
 
 def test_natural_rejects_unsupported():
