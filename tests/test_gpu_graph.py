@@ -1,8 +1,9 @@
 """GPU: the step recorded into a HIP graph.  After the prepare calls no entry point allocates,
 copies between host and device or clears memory, so the whole warm-up step (permute q, k, v;
 dense attention with entropy; mask; schedule; scheduled block-sparse attention; unpermute) and
-the natural-order reuse step can be captured once and replayed, and so can the variants (the
-1D-distance mask, its schedule, the fp8-score sparse call).  Every replay, on fresh inputs copied
+the natural-order reuse step and the natural-order warm-up (one call) can be captured once and
+replayed, and so can the variants (the 1D-distance mask, its schedule, the fp8-score sparse
+call).  Every replay, on fresh inputs copied
 into the captured buffers (eager work and a synchronisation before each), equals the same calls
 made eagerly on those inputs bit for bit."""
 import math
@@ -62,6 +63,16 @@ def test_step_graph_replays_equal_eager():
     def reuse_step():
         t.block_sparse_attn_natural(q, k, v, cnt, idx, F, H, W, sm_scale=sc, out=onat)
 
+    # the warm-up step as one call on natural-order tensors (its own outputs)
+    onw = torch.empty_like(q)
+    entn = torch.empty_like(ent)
+    cntn = torch.empty_like(cnt)
+    idxn = torch.zeros_like(idx)
+
+    def natural_warmup():
+        t.dense_attn_entropy_mask_natural(q, k, v, F, H, W, TAU, GAMMA, sc, out=onw, ent_out=entn, kv_count=cntn,
+                                          kv_index=idxn)
+
     def load(seed):
         for dst, src in zip((q, k, v), _inputs(torch, seed)):
             dst.copy_(src)
@@ -73,15 +84,18 @@ def test_step_graph_replays_equal_eager():
         load(seed)
         warmup_step()
         reuse_step()
+        natural_warmup()
         torch.cuda.synchronize()
-        ref[seed] = [x.clone() for x in (od, ent, cnt, idx, order, o, onat)]
+        ref[seed] = [x.clone() for x in (od, ent, cnt, idx, order, o, onat, onw, entn, cntn, idxn)]
     say("eager density %.3f" % float(ref[SEEDS[0]][2].float().mean() / nkb))
 
-    g_warm, g_reuse = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    g_warm, g_reuse, g_nat = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_warm):
         warmup_step()
     with torch.cuda.graph(g_reuse):
         reuse_step()
+    with torch.cuda.graph(g_nat):
+        natural_warmup()
     torch.cuda.synchronize()
 
     for rep, seed in enumerate(SEEDS + SEEDS[::-1]):
@@ -89,7 +103,7 @@ def test_step_graph_replays_equal_eager():
         load(seed)
         g_warm.replay()
         torch.cuda.synchronize()
-        r_od, r_ent, r_cnt, r_idx, r_order, r_o, r_onat = ref[seed]
+        r_od, r_ent, r_cnt, r_idx, r_order, r_o, r_onat, r_onw, r_entn, r_cntn, r_idxn = ref[seed]
         assert torch.equal(od, r_od), "dense o, replay %d" % rep
         assert torch.equal(ent, r_ent), "entropy, replay %d" % rep
         assert _lists_equal(torch, cnt, idx, r_cnt, r_idx), "block lists, replay %d" % rep
@@ -99,6 +113,11 @@ def test_step_graph_replays_equal_eager():
         g_reuse.replay()
         torch.cuda.synchronize()
         assert torch.equal(onat, r_onat), "natural-order reuse o, replay %d" % rep
+        g_nat.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(onw, r_onw), "natural-order warm-up o, replay %d" % rep
+        assert torch.equal(entn, r_entn), "natural-order warm-up entropy, replay %d" % rep
+        assert _lists_equal(torch, cntn, idxn, r_cntn, r_idxn), "natural-order warm-up lists, replay %d" % rep
     assert np.isfinite(o.float().cpu().numpy()).all()
 
 
