@@ -101,3 +101,26 @@ def uniform_ints(seed: int, n: int, lo: int, hi: int) -> np.ndarray:
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(ROOT_SEED + 2000 + seed)))
     n = min(n, hi - lo)
     return np.sort(g.choice(np.arange(lo, hi), size=n, replace=False)).astype(np.int32)
+
+
+def normal_chunk(seed: int, which: int, chunk: int, rows: int, D: int) -> np.ndarray:
+    """Seeded N(0, 1) float32 [rows][D]: chunk `chunk` of tensor `which` (its own child stream,
+    SeedSequence(root + 3000 + seed, spawn_key=(which, chunk))), so any chunk of a very large
+    tensor can be drawn alone and chunks can be drawn in parallel."""
+    ss = np.random.SeedSequence(ROOT_SEED + 3000 + seed, spawn_key=(which, chunk))
+    out = np.empty((rows, D), dtype=np.float32)
+    np.random.Generator(np.random.PCG64(ss)).standard_normal(out=out, dtype=np.float32)
+    return out
+
+
+def normal_rows(seed: int, which: int, N: int, D: int, chunk_rows: int = 1 << 18):
+    """Tensor `which` of N(0, 1) float32 rows [N][D] in chunks of chunk_rows rows (the last one
+    shorter): yields (first_row, chunk) in row order, drawing up to 16 chunks at a time in
+    parallel.  Chunk c is normal_chunk(seed, which, c, ...)."""
+    starts = list(range(0, N, chunk_rows))
+    with ThreadPoolExecutor(max_workers=_threads()) as ex:
+        for i in range(0, len(starts), _threads()):
+            batch = starts[i:i + _threads()]
+            arrs = ex.map(lambda s: normal_chunk(seed, which, s // chunk_rows, min(chunk_rows, N - s), D), batch)
+            for s, a in zip(batch, arrs):
+                yield s, a

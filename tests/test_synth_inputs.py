@@ -33,3 +33,22 @@ def test_entropy_predicts_effective_key_count():
     # and the budget exp(H) is within a constant factor of k90 for most queries
     ratio = np.log(k90) - H
     assert np.percentile(ratio, 95) - np.percentile(ratio, 5) < 2.5
+
+
+def test_normal_rows_chunks_are_reproducible_and_independent():
+    # the chunked generator behind the largest-head tests: every chunk is normal_chunk drawn
+    # alone (so a test can redraw any rows it checks), chunks and tensors differ, and the values
+    # are standard normal
+    N, D, rows = 1000, 8, 96
+    got = list(synth.normal_rows(5, 1, N, D, chunk_rows=rows))
+    assert [s for s, _ in got] == list(range(0, N, rows))
+    assert sum(a.shape[0] for _, a in got) == N and all(a.dtype == np.float32 for _, a in got)
+    for s, a in got:
+        assert np.array_equal(a, synth.normal_chunk(5, 1, s // rows, min(rows, N - s), D))
+    full = np.concatenate([a for _, a in got])
+    again = np.concatenate([a for _, a in synth.normal_rows(5, 1, N, D, chunk_rows=rows)])
+    assert np.array_equal(full, again)
+    other = np.concatenate([a for _, a in synth.normal_rows(5, 2, N, D, chunk_rows=rows)])
+    assert not np.array_equal(full, other)
+    assert not np.array_equal(got[0][1], got[1][1][:rows])
+    assert abs(float(full.mean())) < 0.05 and abs(float(full.std()) - 1.0) < 0.05
