@@ -472,7 +472,9 @@ tra_status check_natural(int F, int H, int W, int D, tra_dtype dt, int tile_h, i
     if (st != TRA_OK) return st;
     if (dt != TRA_BF16 || D != 128) return TRA_ERR_UNSUPPORTED;
     if (W % 4 != 0 || tile_w % 4 != 0) return TRA_ERR_UNSUPPORTED;
-    if ((int64_t)g.N * D * 2 > (int64_t)0xFFFFFFFF) return TRA_ERR_UNSUPPORTED;  // 32-bit row offsets per head
+    // the natural-order sparse kernel forms each copy's byte offset within a head in 32-bit
+    // signed arithmetic (natural row * 256 + the offset within the run)
+    if ((int64_t)g.N * D * 2 > (int64_t)INT32_MAX) return TRA_ERR_UNSUPPORTED;
     return TRA_OK;
 }
 

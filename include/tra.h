@@ -313,7 +313,8 @@ tra_status tra_dense_attn_entropy_mask(const void *q, const void *k, const void 
  * table too).
  * Supported: bf16, D = 128, W and tile_w multiples of 4 (then every aligned
  * group of four tile-major positions is a run of four natural rows), N*D*2 <
- * 2^32; sparse: block_q = 128, block_k = 64.  Anything else returns
+ * 2^31 (as tra_block_sparse_attn's bf16 limit); sparse: block_q = 128,
+ * block_k = 64.  Anything else returns
  * TRA_ERR_UNSUPPORTED before any HIP call.  The first call for a geometry
  * builds and uploads the map (N/4 int32 natural row indices) synchronously
  * (tra_natural_prepare does that ahead of time); it stays in the per-device

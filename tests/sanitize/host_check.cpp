@@ -294,6 +294,17 @@ int main() {
         CHECK(tra_dense_attn_entropy(q.data(), k.data(), v.data(), o.data(), nullptr, nullptr, 1, big, D, TRA_BF16,
                                      0.088f, nullptr) == TRA_OK,
               "dense, 2^31-byte head (global loads: no buffer limit)");
+        // the natural-order calls too (the sparse one forms its copy offsets within a head in 32-bit
+        // signed arithmetic): 1 x 2048 x 4096 = 2^23 tokens is refused, 1 x 2047 x 4096 accepted
+        CHECK(tra_natural_prepare(1, 2048, 4096, 8, 8) == TRA_ERR_UNSUPPORTED, "natural prepare, 2^31-byte head");
+        CHECK(tra_block_sparse_attn_natural(q.data(), k.data(), v.data(), o.data(), nullptr, cnt.data(), idx.data(), 1,
+                                            1, 2048, 4096, D, TRA_BF16, 0.088f, 128, 64, 8, 8,
+                                            nullptr) == TRA_ERR_UNSUPPORTED,
+              "natural sparse, 2^31-byte head");
+        CHECK(tra_dense_attn_entropy_natural(q.data(), k.data(), v.data(), o.data(), nullptr, nullptr, 1, 1, 2048, 4096,
+                                             D, TRA_BF16, 0.088f, 8, 8, nullptr) == TRA_ERR_UNSUPPORTED,
+              "natural dense, 2^31-byte head");
+        CHECK(tra_natural_prepare(1, 2047, 4096, 8, 8) == TRA_OK, "natural prepare, largest head");
         CHECK(tra_dense_attn_entropy(nullptr, k.data(), v.data(), o.data(), nullptr, nullptr, 1, N, D, TRA_BF16,
                                      0.088f, nullptr) == TRA_ERR_INVALID_ARG,
               "null q");
