@@ -10,7 +10,8 @@ is the last q-block (127 rows).  Every q-block's list holds its own two k-blocks
 k-block and the last three, so every q-block copies the tiles at the top of the head's offset
 range, between its products and at the step start.  bf16 in the schedule's order, and fp8
 scores, on sampled q-blocks of both heads against the oracle (the oracle sees each sampled
-q-block's queries against exactly its retained keys, from the same seeded rows).
+q-block's queries against exactly its retained keys, from the same seeded rows).  Then the
+tile-major permutation of those tensors, on seeded rows bit for bit.
 """
 import functools
 import math
@@ -122,5 +123,22 @@ def test_sparse_largest_head(orc):
                 worst[kind == "fp8"] = max(worst[kind == "fp8"], err)
         say("  head %d: sampled q-blocks %s match the oracle" % (h, blocks))
     say("  max-abs bf16 %.3g, fp8 %.3g" % tuple(worst))
-    del o, L, o8, L8, v, cnt
+    del o, L, o8, L8, cnt
+    torch.cuda.empty_cache()
+
+    # the permutation at this size (8 x 8 tiles; W = 4097 leaves a clipped column of 1-wide
+    # tiles): seeded tile-major rows of both heads, bit for bit the generator's rows at the
+    # oracle's enumerated order
+    y = t.tile_major_permute(v, 1, HH, WW)
+    torch.cuda.synchronize()
+    perm = orc.tile_major_order(1, HH, WW)
+    pos = np.unique(np.concatenate([synth.uniform_ints(SEED + 1, 2000, 0, N), [0, N - 1]])).astype(np.int64)
+    for h in range(OUTER):
+        got = y[h].index_select(0, torch.from_numpy(pos).to(dev)).cpu()
+        src = np.sort(perm[pos])
+        want = torch.from_numpy(_rows(3 * h + 2, src)).to(torch.bfloat16)
+        order_back = np.argsort(np.argsort(perm[pos]))
+        assert torch.equal(got.view(torch.int16), want[torch.from_numpy(order_back)].view(torch.int16)), "head %d" % h
+    say("  permutation: %d seeded rows of each head bit for bit" % len(pos))
+    del y, v
     torch.cuda.empty_cache()
