@@ -20,7 +20,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "tra_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# TRA_ORACLE_LIB names another build of tra_oracle.c to load (the planted-mistake tests load
+# deliberately broken copies this way, in a process of their own)
+_LIB = os.environ.get("TRA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
