@@ -14,7 +14,8 @@ bit the tile-major call; against the oracle, under the oracle's mask, on every q
 mask row the oracle fixes).  And the 1D-distance mask (bit for bit against the oracle) with
 the fp8-score sparse call in the schedule's order on its block_q = 128 lists (against the
 oracle on the decoded fp8 and bf16 inputs, lse within 1e-3 plus the fp8 instruction's
-score-error bound).  The fixed
+score-error bound).  And dense attention + entropy (bf16 or fp32, D = 64 or 128) on every query
+against the oracle, with the permutation and its inverse bit for bit.  The fixed
 cases elsewhere pin the shapes that matter most; these reach combinations nobody chose by
 hand."""
 import math
@@ -213,3 +214,44 @@ def test_random_geometry_mask1d_and_fp8(orc, seed):
         assert np.all(d <= LSE_TOL + bound[fin]), "head %d fp8 lse beyond the bound" % h
         worst, worst_lse = max(worst, err), max(worst_lse, float(d.max()) if d.size else 0.0)
     say("  fp8 sparse max-abs %.3g, lse %.3g" % (worst, worst_lse))
+
+
+@pytest.mark.parametrize("seed", range(1300, 1308))
+def test_random_geometry_dense_and_permutation(orc, seed):
+    # dense attention + entropy (bf16 or fp32, D = 64 or 128) on the tile-major permuted inputs of a
+    # random geometry and tile shape: o, entropy and lse of every query of both heads against the
+    # oracle's fp64 attention; the permutation and its inverse bit for bit against the oracle's
+    # enumerated order
+    torch = torch_mod()
+    t = tra()
+    dev = device()
+    F, H, W, th, tw, _, _, _, _ = _case(seed)
+    N = F * H * W
+    rng = np.random.default_rng(seed + 7919)
+    Dh = int(rng.choice([64, 128]))
+    dt = str(rng.choice(["bf16", "f32"]))
+    say("random dense", seed, (F, H, W), "tile", (th, tw), "D", Dh, dt)
+    q, k, v = synth.qkv(seed, OUTER, F, H, W, Dh)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    qc, kc, vc = (torch.from_numpy(x).to(tdt) for x in (q, k, v))
+    perm = orc.tile_major_order(F, H, W, th, tw)
+    qp, kp, vp = (t.tile_major_permute(x.to(dev), F, H, W, th, tw) for x in (qc, kc, vc))
+    back = t.tile_major_unpermute(qp, F, H, W, th, tw)
+    torch.cuda.synchronize()
+    bits = (lambda x: x.view(torch.int16)) if dt == "bf16" else (lambda x: x.view(torch.int32))
+    assert torch.equal(bits(qp.cpu()), bits(qc[:, torch.from_numpy(perm)])), "permutation"
+    assert torch.equal(bits(back.cpu()), bits(qc)), "round trip"
+    scale = 1.0 / math.sqrt(Dh)
+    o, Hh, L = t.dense_attn_entropy(qp, kp, vp, scale, entropy=True, lse=True)
+    torch.cuda.synchronize()
+    o_h, H_h, L_h = o.float().cpu().numpy(), Hh.cpu().numpy(), L.cpu().numpy()
+    worst = [0.0, 0.0, 0.0]
+    for h in range(OUTER):
+        qh, kh, vh = (orc.permute(np64(x[h]), perm) for x in (qc, kc, vc))
+        ro, rH, rL = orc.attention(qh, kh, vh, scale)
+        err, _ = check_output(o_h[h], ro, dt)
+        e_ent = float(np.max(np.abs(H_h[h] - rH)))
+        e_lse = float(np.max(np.abs(L_h[h] - rL)))
+        assert e_ent <= 1e-3 and e_lse <= LSE_TOL, "head %d entropy %.3g lse %.3g" % (h, e_ent, e_lse)
+        worst = [max(worst[0], err), max(worst[1], e_ent), max(worst[2], e_lse)]
+    say("  dense vs oracle: max-abs out %.3g, entropy %.3g, lse %.3g" % tuple(worst))
